@@ -1,0 +1,203 @@
+"""Reference oracle (fp64, CPU) for the hybrid sliding/global attention layer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``.  The HIP library never imports,
+links or calls it, and it shares no code with the HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over
+independent rows); this module only compiles it with gcc and marshals numpy
+arrays into it.  bfloat16 tensors are passed as their raw uint16 bit patterns.
+
+Source of each definition (the page and section it restates):
+  * head sizes 256 / 512, full attention on every fifth layer, RoPE theta
+    1e4 / 1e6, 35 layers sharing 15 KV caches: onnxruntime-genai feature
+    request "Support for Google Gemma 4 model family", sections
+    "Variable Attention Head Dimensions", "KV Cache Sharing",
+    "Gemma 4 Model Details";
+  * K=V aliasing in sliding layers (V is the raw key projection): the
+    Gemma-4 weight loader page (spark_model/weight_loader/gemma4.rs),
+    comment in ``supports_tp``; SGLang PR "Support encoder-free unified
+    Text/Vision/Audio model", attention_k_eq_v shard duplication;
+  * softmax attention with causal / sliding-window masks, RoPE and GQA:
+    standard definitions; the readings taken where the pages are silent
+    (window counts W keys including self, scale 1/sqrt(D), rotate-half
+    pairing, raw keys in the cache) are listed in the design notes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+# HSG_ORACLE_LIB lets the mutation test load a deliberately broken copy.
+_LIB_OVERRIDE = os.environ.get("HSG_ORACLE_LIB")
+_LIB_PATH = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math, OpenMP) into liboracle.so."""
+    global _lib
+    if _LIB_OVERRIDE:
+        return _LIB_PATH
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+        _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.orc_rope_inv_freq.argtypes = [ctypes.c_int32, ctypes.c_double, _f64p]
+        lib.orc_rope.argtypes = [_f64p, ctypes.c_int32, ctypes.c_double, ctypes.c_double, _f64p]
+        lib.orc_attention_row.argtypes = [_u16p, _u16p, _u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_double, ctypes.c_double, _f64p, _f64p]
+        lib.orc_attention_row.restype = ctypes.c_int
+        lib.orc_prefill.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_double, ctypes.c_double, _u16p, _u16p, _u16p,
+                                                           _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
+        lib.orc_prefill.restype = ctypes.c_int
+        lib.orc_decode.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_double, ctypes.c_double, _u16p, _u16p, _u16p,
+                                                          _i32p, _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
+        lib.orc_decode.restype = ctypes.c_int
+        lib.orc_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray], t):
+    if a is None:
+        return ctypes.cast(None, t)
+    return a.ctypes.data_as(t)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bfloat16 tensors are passed as uint16 bit patterns")
+    return a
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def inv_freq(D: int, theta: float) -> np.ndarray:
+    out = np.empty(D // 2, np.float64)
+    _load().orc_rope_inv_freq(D, theta, _ptr(out, _f64p))
+    return out
+
+
+def rope(x: np.ndarray, theta: float, pos: float) -> np.ndarray:
+    """Rotate-half RoPE of one fp64 D-vector at position ``pos``."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _load().orc_rope(_ptr(x, _f64p), x.shape[0], theta, float(pos), _ptr(y, _f64p))
+    return y
+
+
+def attention_row(q: np.ndarray, k_slice: np.ndarray, v_slice: Optional[np.ndarray], pos: int, length: int,
+                  window: int, theta: float, scale: float = 0.0):
+    """One query row over one (batch, kv-head) cache slice.
+
+    Returns ``(weights[length], out[D])``.  ``v_slice=None`` means an aliased
+    layer: the value rows are the raw key rows.
+    """
+    q = _u16(q)
+    k_slice = _u16(k_slice)
+    v_slice = k_slice if v_slice is None else _u16(v_slice)
+    D = q.shape[-1]
+    w = np.empty(length, np.float64)
+    o = np.empty(D, np.float64)
+    rc = _load().orc_attention_row(_ptr(q, _u16p), _ptr(k_slice, _u16p), _ptr(v_slice, _u16p), D, pos, length,
+                                   window, theta, scale, _ptr(w, _f64p), _ptr(o, _f64p))
+    if rc != 0:
+        raise ValueError("oracle: invalid attention row")
+    return w, o
+
+
+def prefill(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], window: int, theta: float, scale: float = 0.0,
+            rows: Optional[Sequence[int]] = None, nthreads: int = 0) -> np.ndarray:
+    """Prefill attention; q [B,S,Hq,D], k/v [B,Hkv,Lmax,D] (v None = aliased).
+
+    Returns fp64 [B,S,Hq,D], or [len(rows), D] for flattened rows b*S*Hq+s*Hq+h.
+    """
+    q, k = _u16(q), _u16(k)
+    v = None if v is None else _u16(v)
+    B, S, Hq, D = q.shape
+    _, Hkv, Lmax, Dk = k.shape
+    if Dk != D or (v is not None and v.shape != k.shape):
+        raise ValueError("shape mismatch")
+    if rows is None:
+        out = np.empty((B, S, Hq, D), np.float64)
+        r, n = None, -1
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        n = r.shape[0]
+        out = np.empty((n, D), np.float64)
+    rc = _load().orc_prefill(B, S, Hq, Hkv, D, Lmax, window, theta, scale, _ptr(q, _u16p), _ptr(k, _u16p),
+                            _ptr(v, _u16p), _ptr(r, _i64p), n, _ptr(out, _f64p), nthreads)
+    if rc != 0:
+        raise ValueError("oracle: invalid prefill arguments")
+    return out
+
+
+def decode(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], kv_len: np.ndarray, window: int, theta: float,
+           scale: float = 0.0, rows: Optional[Sequence[int]] = None, nthreads: int = 0) -> np.ndarray:
+    """Decode attention; q [B,Hq,D], k/v [B,Hkv,Lmax,D], kv_len [B] (host)."""
+    q, k = _u16(q), _u16(k)
+    v = None if v is None else _u16(v)
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, Dk = k.shape
+    if Dk != D or (v is not None and v.shape != k.shape):
+        raise ValueError("shape mismatch")
+    kl = np.ascontiguousarray(kv_len, dtype=np.int32)
+    if rows is None:
+        out = np.empty((B, Hq, D), np.float64)
+        r, n = None, -1
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        n = r.shape[0]
+        out = np.empty((n, D), np.float64)
+    rc = _load().orc_decode(B, Hq, Hkv, D, Lmax, window, theta, scale, _ptr(q, _u16p), _ptr(k, _u16p),
+                            _ptr(v, _u16p), _ptr(kl, _i32p), _ptr(r, _i64p), n, _ptr(out, _f64p), nthreads)
+    if rc != 0:
+        raise ValueError("oracle: invalid decode arguments")
+    return out
+
+
+def stack_prefill(layers: Sequence[dict], qs: Sequence[np.ndarray], k_caches: Sequence[Optional[np.ndarray]],
+                  v_caches: Sequence[Optional[np.ndarray]], rows: Optional[Sequence[int]] = None,
+                  nthreads: int = 0) -> list:
+    """Prefill over a stack of layers with KV-cache sharing.
+
+    Each layer dict carries ``head_dim, rope_theta, window, kv_alias,
+    kv_source_layer``.  A layer with ``kv_source_layer >= 0`` owns no cache
+    and reads the source layer's buffers (N layers -> M unique caches, the
+    feature request's "KV Cache Sharing" section); an aliased layer reads its
+    values from the key buffer.
+    """
+    outs = []
+    for li, d in enumerate(layers):
+        src = li if d["kv_source_layer"] < 0 else d["kv_source_layer"]
+        k = k_caches[src]
+        v = None if d["kv_alias"] else v_caches[src]
+        outs.append(prefill(qs[li], k, v, d["window"], d["rope_theta"], d.get("scale", 0.0), rows=rows,
+                            nthreads=nthreads))
+    return outs
