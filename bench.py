@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid sliding/global attention hot path on one MI355X.
+
+A step is one pass of the prefill path -- descriptor validation, key-RoPE
+pass, fused Q-RoPE + flash attention, fp32 epilogue -- over the full-attention
+prefill workload (batch 1, 4096 tokens, 8 query / 2 kv heads, head size 512,
+causal, separate K and V, RoPE theta 1e6).  Prints ONE JSON line.
+
+The line also carries:
+  roofline      the attention kernel's algorithmic FLOPs per launch / its
+                average duration (HIP events recorded around that kernel on
+                the stream it runs on) against the bf16 dense MFMA peak;
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
+                same workload;
+  decode        batched decode (64 sequences x 8192 cached tokens, full layer
+                head size 512 plus sliding K=V layer head size 256): KV bytes
+                per second of the split-K kernel against HBM peak.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s and decode KV GB/s, as % of MI355X peak"
+PEAK_BF16_TFLOPS = 2500.0  # dense MFMA bf16
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it covers this kernel build."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t.get(kernel)
+        return None if e is None else e.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def time_calls(fn, steps, warmup, flush=None):
+    """Average wall time per call (events around each call) and per main kernel (profile events)."""
+    import torch
+    from hybrid_sliding_global_amd import _lib
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    tot_call = tot_kern = 0.0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        c0, c1, k0, k1 = evs[i]
+        _lib.set_profile_events(k0, k1)
+        c0.record()
+        fn()
+        c1.record()
+        _lib.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    for c0, c1, k0, k1 in evs:
+        tot_call += c0.elapsed_time(c1)
+        tot_kern += k0.elapsed_time(k1)
+    return tot_call / steps, tot_kern / steps
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    from hybrid_sliding_global_amd import Stack, inputs
+    from hybrid_sliding_global_amd import workloads as wl
+    w = wl.workloads()[2]
+    d = w.layers[0]
+    S, Hq, Hkv, D = w.seq_len, d["num_q_heads"], d["num_kv_heads"], d["head_dim"]
+    q_h = inputs.normal_bf16([2, 0, inputs.TENSOR_Q], (1, S, Hq, D))
+    k_h = inputs.normal_bf16([2, 0, inputs.TENSOR_K], (1, Hkv, S, D))
+    v_h = inputs.normal_bf16([2, 0, inputs.TENSOR_V], (1, Hkv, S, D))
+    q, k, v = dev(q_h), dev(k_h), dev(v_h)
+    st = Stack(w.layers)
+    out = torch.empty((1, S, Hq, D), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(st.prefill_workspace_bytes(0, 1, S), dtype=torch.uint8, device="cuda:0")
+    flops = wl.prefill_flops(S, Hq, D, 0)
+
+    def step():
+        st.prefill(0, q, [k], [v], out=out, workspace=ws)
+
+    # timed region: K steps bracketed by synchronize
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    _, kern_ms = time_calls(step, steps, 2)
+    return dict(flops=flops, ms_per_step=ms_per_step, wall=wall, kern_ms=kern_ms, q=q_h, k=k_h, v=v_h, w=w)
+
+
+def cpu_baseline(pre, budget_s=15.0):
+    """fp64 oracle on a bounded, position-spread sample of the prefill rows."""
+    import oracle
+    from hybrid_sliding_global_amd import workloads as wl
+    oracle.build(force=False)
+    w = pre["w"]
+    d = w.layers[0]
+    S, Hq, D = w.seq_len, d["num_q_heads"], d["head_dim"]
+    rng = np.random.default_rng(0)
+    # grow the sample until it takes a few seconds, then extrapolate to the budget
+    n = 8
+    while True:
+        pos = np.sort(rng.integers(0, S, size=n))
+        heads = rng.integers(0, Hq, size=n)
+        rows = pos * Hq + heads
+        t0 = time.perf_counter()
+        oracle.prefill(pre["q"], pre["k"], pre["v"], 0, d["rope_theta"], rows=rows)
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or n >= 1 << 16:
+            break
+        n *= 2
+    flops = float(sum(4 * D * (int(p) + 1) for p in pos))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "%d query rows (uniform positions and heads) of the 4096-token full-attention prefill, "
+                      "fp64, %.1f s" % (n, dt)}
+
+
+def bench_decode(steps, warmup):
+    import torch
+    from hybrid_sliding_global_amd import Stack, inputs
+    from hybrid_sliding_global_amd import workloads as wl
+    w = wl.workloads()[3]
+    B, L = w.batch, w.kv_len
+    kv = np.full(B, L, np.int32)
+    kl = torch.from_numpy(kv).to("cuda:0")
+    flush_buf = torch.empty(1 << 29, dtype=torch.uint8, device="cuda:0")  # 512 MiB > the 256 MB MALL
+
+    def flush():
+        flush_buf.fill_(1)
+
+    res = {}
+    total_bytes = 0
+    total_ms = 0.0
+    for li, d in enumerate(w.layers):
+        D, Hq, Hkv = d["head_dim"], d["num_q_heads"], d["num_kv_heads"]
+        q = dev(inputs.normal_bf16([3, li, inputs.TENSOR_Q], (B, Hq, D)))
+        k = dev(inputs.normal_bf16([3, li, inputs.TENSOR_K], (B, Hkv, L, D)))
+        v = None if d["kv_alias"] else dev(inputs.normal_bf16([3, li, inputs.TENSOR_V], (B, Hkv, L, D)))
+        st = Stack([d])
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(st.decode_workspace_bytes(0, B, L), dtype=torch.uint8, device="cuda:0")
+
+        def step():
+            st.decode(0, q, [k], [v], kl, L, out=out, workspace=ws)
+
+        call_ms, kern_ms = time_calls(step, steps, warmup, flush=flush)
+        nbytes = wl.decode_bytes(kv, Hq, Hkv, D, d["window"], bool(d["kv_alias"]))
+        name = "full" if d["kind"] == wl.FULL else "sliding"
+        res[name] = {"bytes": nbytes, "ms_per_call": call_ms, "kernel_ms": kern_ms,
+                     "GB/s": nbytes / (call_ms * 1e-3) / 1e9, "kernel_GB/s": nbytes / (kern_ms * 1e-3) / 1e9}
+        total_bytes += nbytes
+        total_ms += call_ms
+        del q, k, v
+    full = res["full"]
+    return {
+        "workload": "decode_b64_l8192 (full hd512 Hq8/Hkv2 + sliding hd256 W1024 K=V)",
+        "value": total_bytes / (total_ms * 1e-3) / 1e9, "unit": "GB/s", "layers": res,
+        "roofline": {"bound": "hbm", "achieved": full["kernel_GB/s"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": full["kernel_GB/s"] / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("k_decode<512,false,2>")},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X", file=sys.stderr)
+        sys.exit(1)
+    log("prefill: full-attention layer B=1 S=4096 Hq=8 Hkv=2 D=512")
+    pre = bench_prefill(args.steps, args.warmup)
+    tflops = pre["flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
+    kern_tflops = pre["flops"] / (pre["kern_ms"] * 1e-3) / 1e12
+    log("prefill: %.3f ms/step (%.1f TFLOP/s), attention kernel %.3f ms (%.1f TFLOP/s)" %
+        (pre["ms_per_step"], tflops, pre["kern_ms"], kern_tflops))
+    line = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": pre["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)",
+        "config": {"workload": "full_prefill_s4096", "batch": 1, "seq_len": 4096, "q_heads": 8, "kv_heads": 2,
+                   "head_dim": 512, "window": 0, "rope_theta": 1e6, "kv_alias": False,
+                   "algorithmic_flops": pre["flops"]},
+        "roofline": {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_prefill<512,32,2>")},
+    }
+    if not args.no_decode:
+        log("decode: B=64 L=8192")
+        line["decode"] = bench_decode(max(5, args.steps // 2), 2)
+        log("decode: %.1f GB/s (full-layer kernel %.1f GB/s)" %
+            (line["decode"]["value"], line["decode"]["layers"]["full"]["kernel_GB/s"]))
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on sampled rows")
+        line["cpu_baseline"] = cpu_baseline(pre)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,253 @@
+// C-ABI entry points of libgemma4_attn.so (declared in include/gemma4_attn.h).
+//
+// Host-side work only: descriptor validation, resolution of the KV-cache
+// source layer (N layers reading M < N caches, the sharing map the
+// onnxruntime-genai Gemma 4 feature request asks for under "What Would Need
+// to Change"), workspace sizing and dispatch to the kernel launchers.  The
+// validation and sizing functions never call the HIP runtime, so they can
+// be exercised on a machine without a GPU.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gemma4_attn.h"
+#include "g4_internal.h"
+
+#define G4_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local g4::ProfileEvents g_profile;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return G4_OK;
+}
+
+// Checks of one descriptor on its own.
+int check_desc(const g4_layer_desc& d, int idx) {
+  if (d.kind != G4_SLIDING && d.kind != G4_FULL) return fail(G4_ERR_UNSUPPORTED, "layer %d: kind %d", idx, d.kind);
+  if (d.head_dim != 256 && d.head_dim != 512)
+    return fail(G4_ERR_UNSUPPORTED, "layer %d: head_dim %d (supported: 256, 512)", idx, d.head_dim);
+  if (d.num_q_heads < 1 || d.num_kv_heads < 1)
+    return fail(G4_ERR_INVALID_ARG, "layer %d: head counts %d/%d", idx, d.num_q_heads, d.num_kv_heads);
+  if (d.num_q_heads % d.num_kv_heads != 0)
+    return fail(G4_ERR_UNSUPPORTED, "layer %d: num_q_heads %d not a multiple of num_kv_heads %d", idx,
+                d.num_q_heads, d.num_kv_heads);
+  if (d.kind == G4_SLIDING && d.window <= 0)
+    return fail(G4_ERR_INVALID_ARG, "layer %d: sliding layer needs window > 0 (got %d)", idx, d.window);
+  if (d.kind == G4_FULL && d.window != 0)
+    return fail(G4_ERR_INVALID_ARG, "layer %d: full layer must have window 0 (got %d)", idx, d.window);
+  if (d.kv_alias != 0 && d.kv_alias != 1) return fail(G4_ERR_INVALID_ARG, "layer %d: kv_alias %d", idx, d.kv_alias);
+  if (!(d.rope_theta > 0.0) || !std::isfinite(d.rope_theta))
+    return fail(G4_ERR_INVALID_ARG, "layer %d: rope_theta %g", idx, d.rope_theta);
+  if (!(d.scale >= 0.f) || !std::isfinite(d.scale)) return fail(G4_ERR_INVALID_ARG, "layer %d: scale %g", idx, d.scale);
+  return G4_OK;
+}
+
+// Full check of layer `idx` within its stack, including its cache source.
+int check_layer(const g4_layer_desc* layers, int32_t n_layers, int32_t idx) {
+  if (!layers) return fail(G4_ERR_INVALID_ARG, "layers is NULL");
+  if (n_layers < 1) return fail(G4_ERR_INVALID_ARG, "n_layers %d", n_layers);
+  if (idx < 0 || idx >= n_layers) return fail(G4_ERR_INVALID_ARG, "layer %d out of range [0, %d)", idx, n_layers);
+  const g4_layer_desc& d = layers[idx];
+  int rc = check_desc(d, idx);
+  if (rc) return rc;
+  const int s = d.kv_source_layer;
+  if (s == -1) return G4_OK;
+  if (s < 0 || s >= idx)
+    return fail(G4_ERR_BAD_SOURCE, "layer %d: kv_source_layer %d must be -1 or an earlier layer", idx, s);
+  const g4_layer_desc& src = layers[s];
+  rc = check_desc(src, s);
+  if (rc) return rc;
+  if (src.kv_source_layer != -1)
+    return fail(G4_ERR_BAD_SOURCE, "layer %d: source layer %d does not own a cache", idx, s);
+  if (src.head_dim != d.head_dim || src.num_kv_heads != d.num_kv_heads || src.kv_alias != d.kv_alias)
+    return fail(G4_ERR_BAD_SOURCE, "layer %d: source layer %d has head_dim/num_kv_heads/kv_alias %d/%d/%d, needs %d/%d/%d",
+                idx, s, src.head_dim, src.num_kv_heads, src.kv_alias, d.head_dim, d.num_kv_heads, d.kv_alias);
+  return G4_OK;
+}
+
+int source_of(const g4_layer_desc* layers, int32_t idx) {
+  return layers[idx].kv_source_layer < 0 ? idx : layers[idx].kv_source_layer;
+}
+
+float resolved_scale(const g4_layer_desc& d) {
+  return d.scale > 0.f ? d.scale : (float)(1.0 / std::sqrt((double)d.head_dim));
+}
+
+// The decode kernel maps the query heads of one kv head onto the 16 columns
+// of a 16x16x32 MFMA.
+constexpr int kMaxDecodeGroup = 16;
+
+}  // namespace
+
+G4_EXPORT int gemma4_abi_version(void) { return G4_ABI_VERSION; }
+
+G4_EXPORT const char* gemma4_status_string(int status) {
+  switch (status) {
+    case G4_OK: return "G4_OK";
+    case G4_ERR_INVALID_ARG: return "G4_ERR_INVALID_ARG";
+    case G4_ERR_UNSUPPORTED: return "G4_ERR_UNSUPPORTED";
+    case G4_ERR_BAD_SOURCE: return "G4_ERR_BAD_SOURCE";
+    case G4_ERR_WORKSPACE: return "G4_ERR_WORKSPACE";
+    case G4_ERR_HIP: return "G4_ERR_HIP";
+    default: return "G4_ERR_UNKNOWN";
+  }
+}
+
+G4_EXPORT const char* gemma4_last_error(void) { return g_last_error; }
+
+G4_EXPORT int gemma4_validate_layers(const g4_layer_desc* layers, int32_t n_layers) {
+  if (!layers) return fail(G4_ERR_INVALID_ARG, "layers is NULL");
+  if (n_layers < 1) return fail(G4_ERR_INVALID_ARG, "n_layers %d", n_layers);
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const int rc = check_layer(layers, n_layers, i);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+G4_EXPORT int gemma4_kv_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch,
+                              int32_t max_len, size_t* k_bytes, size_t* v_bytes) {
+  int rc = check_layer(layers, n_layers, layer);
+  if (rc) return rc;
+  if (!k_bytes || !v_bytes) return fail(G4_ERR_INVALID_ARG, "output pointer is NULL");
+  if (batch < 1 || max_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, max_len %d", batch, max_len);
+  const g4_layer_desc& d = layers[layer];
+  if (d.kv_source_layer >= 0) {
+    *k_bytes = *v_bytes = 0;
+    return ok();
+  }
+  const size_t bytes = (size_t)batch * d.num_kv_heads * (size_t)max_len * d.head_dim * 2;
+  *k_bytes = bytes;
+  *v_bytes = d.kv_alias ? 0 : bytes;
+  return ok();
+}
+
+G4_EXPORT int gemma4_prefill_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
+                                             int32_t batch, int32_t seq_len, size_t* bytes) {
+  int rc = check_layer(layers, n_layers, layer);
+  if (rc) return rc;
+  if (!bytes) return fail(G4_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || seq_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d", batch, seq_len);
+  const g4_layer_desc& d = layers[layer];
+  *bytes = g4::prefill_workspace(batch, seq_len, d.num_kv_heads, d.head_dim);
+  return ok();
+}
+
+G4_EXPORT int gemma4_decode_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
+                                            int32_t batch, int32_t max_kv_len, size_t* bytes) {
+  int rc = check_layer(layers, n_layers, layer);
+  if (rc) return rc;
+  if (!bytes) return fail(G4_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || max_kv_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, max_kv_len %d", batch, max_kv_len);
+  const g4_layer_desc& d = layers[layer];
+  const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, d.window, max_kv_len);
+  *bytes = g4::decode_workspace(batch, d.num_q_heads, d.head_dim, plan);
+  return ok();
+}
+
+G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                  void* const* k_cache, void* const* v_cache, int32_t batch, int32_t seq_len,
+                                  int32_t max_len, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layer(layers, n_layers, layer);
+  if (rc) return rc;
+  const g4_layer_desc& d = layers[layer];
+  if (batch < 1 || seq_len < 1 || max_len < seq_len)
+    return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d, max_len %d", batch, seq_len, max_len);
+  if ((long long)seq_len * (d.num_q_heads / d.num_kv_heads) > 0x7fffffffLL)
+    return fail(G4_ERR_INVALID_ARG, "seq_len %d too large", seq_len);
+  if (!q || !out || !k_cache) return fail(G4_ERR_INVALID_ARG, "q/out/k_cache is NULL");
+  const int src = source_of(layers, layer);
+  const void* k = k_cache[src];
+  const void* v = d.kv_alias ? k : (v_cache ? v_cache[src] : nullptr);
+  if (!k) return fail(G4_ERR_INVALID_ARG, "k_cache[%d] is NULL", src);
+  if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
+  const size_t need = g4::prefill_workspace(batch, seq_len, d.num_kv_heads, d.head_dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(G4_ERR_WORKSPACE, "prefill workspace %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
+  g4::PrefillLaunch p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.kimg = workspace;
+  p.B = batch;
+  p.S = seq_len;
+  p.Hq = d.num_q_heads;
+  p.Hkv = d.num_kv_heads;
+  p.D = d.head_dim;
+  p.Lmax = max_len;
+  p.W = d.kind == G4_SLIDING ? d.window : 0;
+  p.scale = resolved_scale(d);
+  p.theta = d.rope_theta;
+  const hipError_t e = g4::launch_prefill(p, static_cast<hipStream_t>(stream), g_profile);
+  if (e != hipSuccess) return fail(G4_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                 void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
+                                 int32_t max_len, int32_t max_kv_len, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int rc = check_layer(layers, n_layers, layer);
+  if (rc) return rc;
+  const g4_layer_desc& d = layers[layer];
+  if (batch < 1 || max_kv_len < 1 || max_len < max_kv_len)
+    return fail(G4_ERR_INVALID_ARG, "batch %d, max_len %d, max_kv_len %d", batch, max_len, max_kv_len);
+  if (d.num_q_heads / d.num_kv_heads > kMaxDecodeGroup)
+    return fail(G4_ERR_UNSUPPORTED, "decode supports at most %d query heads per kv head (got %d)", kMaxDecodeGroup,
+                d.num_q_heads / d.num_kv_heads);
+  if (!q || !out || !k_cache || !kv_len) return fail(G4_ERR_INVALID_ARG, "q/out/k_cache/kv_len is NULL");
+  const int src = source_of(layers, layer);
+  const void* k = k_cache[src];
+  const void* v = d.kv_alias ? k : (v_cache ? v_cache[src] : nullptr);
+  if (!k) return fail(G4_ERR_INVALID_ARG, "k_cache[%d] is NULL", src);
+  if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
+  const int W = d.kind == G4_SLIDING ? d.window : 0;
+  const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, W, max_kv_len);
+  const size_t need = g4::decode_workspace(batch, d.num_q_heads, d.head_dim, plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(G4_ERR_WORKSPACE, "decode workspace %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
+  g4::DecodeLaunch p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kv_len = kv_len;
+  p.out = out;
+  p.ws = workspace;
+  p.B = batch;
+  p.Hq = d.num_q_heads;
+  p.Hkv = d.num_kv_heads;
+  p.D = d.head_dim;
+  p.Lmax = max_len;
+  p.W = W;
+  p.alias = d.kv_alias;
+  p.scale = resolved_scale(d);
+  p.theta = d.rope_theta;
+  p.plan = plan;
+  const hipError_t e = g4::launch_decode(p, static_cast<hipStream_t>(stream), g_profile);
+  if (e != hipSuccess) return fail(G4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+G4_EXPORT int gemma4_set_profile_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(G4_ERR_INVALID_ARG, "profile events must both be set or both be NULL");
+  g_profile.before = static_cast<hipEvent_t>(before);
+  g_profile.after = static_cast<hipEvent_t>(after);
+  return ok();
+}

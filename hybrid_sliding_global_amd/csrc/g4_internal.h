@@ -1,0 +1,67 @@
+// Internal host-side interface between the C-ABI layer (g4_api.cpp) and the
+// kernel launchers (g4_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace g4 {
+
+// RoPE frequencies of one layer in revolutions per position:
+// rev[f] = theta^(-2f/D) / (2*pi), f < D/2 (rotate-half pairs (f, f + D/2)).
+struct RopeRev {
+  double rev[256];
+};
+
+void fill_rope_rev(RopeRev* r, int head_dim, double theta);
+
+// Prefill tiling: key tile size per head size, query rows per work-group.
+constexpr int kPrefillRows = 128;
+inline int prefill_key_tile(int head_dim) { return head_dim == 512 ? 32 : 64; }
+
+struct PrefillLaunch {
+  const void* q;      // bf16 [B, S, Hq, D]
+  const void* k;      // bf16 raw keys [B, Hkv, Lmax, D]
+  const void* v;      // bf16 values (== k for an aliased layer)
+  float* out;         // fp32 [B, S, Hq, D]
+  void* kimg;         // workspace: rotated key tiles
+  int B, S, Hq, Hkv, D, Lmax, W;
+  float scale;        // softmax scale (already resolved, > 0)
+  double theta;
+};
+
+// Optional events recorded around the main attention kernel (may be null).
+struct ProfileEvents {
+  hipEvent_t before = nullptr;
+  hipEvent_t after = nullptr;
+};
+
+size_t prefill_workspace(int B, int S, int Hkv, int D);
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const ProfileEvents& ev);
+
+// Decode split-K planning: keys per work-group and number of chunks.
+struct DecodePlan {
+  int chunk;    // keys per work-group (multiple of 32)
+  int nchunks;  // chunks per (batch, kv-head) stream
+};
+DecodePlan plan_decode(int B, int Hkv, int W, int max_kv_len);
+size_t decode_workspace(int B, int Hq, int D, const DecodePlan& plan);
+
+struct DecodeLaunch {
+  const void* q;        // bf16 [B, Hq, D]
+  const void* k;        // bf16 raw keys [B, Hkv, Lmax, D]
+  const void* v;        // bf16 values (== k when aliased)
+  const int32_t* kv_len;  // device [B]
+  float* out;           // fp32 [B, Hq, D]
+  void* ws;
+  int B, Hq, Hkv, D, Lmax, W, alias;
+  float scale;
+  double theta;
+  DecodePlan plan;
+};
+
+hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const ProfileEvents& ev);
+
+}  // namespace g4

@@ -1,0 +1,41 @@
+"""Shared helpers of the GPU parity tests (imported by test modules only)."""
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from hybrid_sliding_global_amd import inputs  # noqa: E402
+
+# Tolerance fixed by the method's bf16-input / fp32-accumulate arithmetic:
+# max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3.
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def to_dev(a: np.ndarray):
+    """uint16 bfloat16 bits -> torch bf16 tensor on cuda:0."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def check(got, want, tag: str, max_abs: float = MAX_ABS, mean_abs: float = MEAN_ABS):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (tag, got.shape, want.shape)
+    assert np.isfinite(got).all(), "%s: non-finite output" % tag
+    err = np.abs(got - want)
+    mx, mn = float(err.max()), float(err.mean())
+    rel = float(np.sqrt((err ** 2).mean() / max((want ** 2).mean(), 1e-30)))
+    print("%s: max_abs %.3e mean_abs %.3e rel_rms %.3e" % (tag, mx, mn, rel), flush=True)
+    assert mx <= max_abs and mn <= mean_abs, "%s: max_abs %.3e mean_abs %.3e" % (tag, mx, mn)
+    return mx, mn
+
+
+def prefill_rows(B, S, Hq, positions, heads=None):
+    """Flattened row indices b*S*Hq + s*Hq + h for the given positions (every b, listed heads)."""
+    heads = range(Hq) if heads is None else heads
+    return np.array([(b * S + s) * Hq + h for b in range(B) for s in positions for h in heads], np.int64)

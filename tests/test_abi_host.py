@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI (include/gemma4_attn.h) -- no GPU needed.
+
+The library must load, export every function the header declares, and reject
+bad descriptors / arguments with the documented status codes before it
+touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_sliding_global_amd import _lib as L
+from hybrid_sliding_global_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemma4_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        import hybrid_sliding_global_amd.build as b
+        b.build()
+    return L.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemma4_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert names, "no functions parsed from the header"
+    assert set(names) == set(L.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert L.abi_version() == 1
+    for code, name in [(0, "G4_OK"), (-1, "G4_ERR_INVALID_ARG"), (-2, "G4_ERR_UNSUPPORTED"),
+                       (-3, "G4_ERR_BAD_SOURCE"), (-4, "G4_ERR_WORKSPACE"), (-5, "G4_ERR_HIP")]:
+        assert L.status_string(code) == name
+
+
+def test_descriptor_layout_matches_header(lib):
+    assert ctypes.sizeof(L.LayerDesc) == 40
+    assert L.LayerDesc.rope_theta.offset == 32 and L.LayerDesc.scale.offset == 28
+
+
+def test_gemma4_stack_validates(lib):
+    assert L.validate_layers(wl.gemma4_stack()) == 0
+
+
+def _one(**kw):
+    d = wl.layer_desc(wl.SLIDING, 256, 8, 1, 1e4, 512, 1)
+    d.update(kw)
+    return d
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=128), L.G4_ERR_UNSUPPORTED),
+    (dict(head_dim=384), L.G4_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=4), L.G4_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=0), L.G4_ERR_INVALID_ARG),
+    (dict(window=0), L.G4_ERR_INVALID_ARG),
+    (dict(window=-3), L.G4_ERR_INVALID_ARG),
+    (dict(kind=wl.FULL, head_dim=512, window=512), L.G4_ERR_INVALID_ARG),
+    (dict(kind=7), L.G4_ERR_UNSUPPORTED),
+    (dict(rope_theta=0.0), L.G4_ERR_INVALID_ARG),
+    (dict(rope_theta=float("nan")), L.G4_ERR_INVALID_ARG),
+    (dict(scale=-1.0), L.G4_ERR_INVALID_ARG),
+    (dict(kv_alias=2), L.G4_ERR_INVALID_ARG),
+])
+def test_bad_descriptor_rejected(lib, kw, code):
+    assert L.validate_layers([_one(**kw)]) == code
+    assert L.last_error() != ""
+
+
+def test_bad_sources_rejected(lib):
+    full = wl.layer_desc(wl.FULL, 512, 8, 2, 1e6, 0, 0)
+    sl = _one()
+    # source must be earlier
+    assert L.validate_layers([_one(kv_source_layer=0)]) == L.G4_ERR_BAD_SOURCE
+    assert L.validate_layers([sl, _one(kv_source_layer=1)]) == L.G4_ERR_BAD_SOURCE
+    assert L.validate_layers([sl, _one(kv_source_layer=5)]) == L.G4_ERR_BAD_SOURCE
+    # source must own its cache
+    assert L.validate_layers([sl, _one(kv_source_layer=0), _one(kv_source_layer=1)]) == L.G4_ERR_BAD_SOURCE
+    # head dim / kv heads / alias must match
+    assert L.validate_layers([full, _one(kv_source_layer=0)]) == L.G4_ERR_BAD_SOURCE
+    assert L.validate_layers([sl, _one(num_q_heads=4, num_kv_heads=2, kv_source_layer=0)]) == L.G4_ERR_BAD_SOURCE
+    assert L.validate_layers([sl, _one(kv_alias=0, kv_source_layer=0)]) == L.G4_ERR_BAD_SOURCE
+    # matching source accepted (query heads may differ)
+    assert L.validate_layers([sl, _one(num_q_heads=4, kv_source_layer=0)]) == 0
+
+
+def test_kv_bytes_and_sharing(lib):
+    stack = wl.gemma4_stack()
+    total_k = total_v = 0
+    for i in range(len(stack)):
+        k, v = L.kv_bytes(stack, i, 1, 2048)
+        total_k += k
+        total_v += v
+        if stack[i]["kv_source_layer"] >= 0:
+            assert k == v == 0
+    # 12 aliased sliding owners (one 1 MiB buffer each) + 3 full owners (K and V, 4 MiB each)
+    assert total_k + total_v == 12 * 2048 * 256 * 2 + 3 * 2 * (2 * 2048 * 512 * 2) == 37748736
+
+
+def test_workspace_sizes(lib):
+    stack = wl.gemma4_stack()
+    assert L.prefill_workspace_bytes(stack, 4, 1, 2048) == 1 * 2 * 2048 * 512 * 2
+    assert L.prefill_workspace_bytes(stack, 0, 1, 2048) == 1 * 1 * 2048 * 256 * 2
+    assert L.prefill_workspace_bytes(stack, 0, 1, 100) == 1 * 1 * 128 * 256 * 2  # padded to the key tile
+    w = L.decode_workspace_bytes(stack, 4, 64, 8192)
+    assert w > 0 and w % 4 == 0
+    with pytest.raises(L.Gemma4Error):
+        L.prefill_workspace_bytes(stack, 4, 0, 2048)
+
+
+def test_compute_calls_reject_bad_arguments_without_gpu(lib):
+    """Argument errors are reported before anything is enqueued (no HIP call)."""
+    stack = wl.gemma4_stack()
+    arr = L.descs(stack)
+    n = len(stack)
+    null_tab = (ctypes.c_void_p * n)()
+    fake = ctypes.c_void_p(0x1000)
+    # NULL q / out
+    assert lib.gemma4_attn_prefill(arr, n, 0, None, null_tab, null_tab, 1, 16, 16, None, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG
+    # seq_len > max_len
+    assert lib.gemma4_attn_prefill(arr, n, 0, fake, null_tab, null_tab, 1, 32, 16, fake, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG
+    # missing cache pointer of the source layer (layer 20 reads layer 13)
+    assert lib.gemma4_attn_prefill(arr, n, 20, fake, null_tab, null_tab, 1, 16, 16, fake, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG
+    assert "k_cache[13]" in L.last_error()
+    # workspace too small
+    tab = (ctypes.c_void_p * n)(*([0x2000] * n))
+    assert lib.gemma4_attn_prefill(arr, n, 4, fake, tab, tab, 1, 2048, 2048, fake, fake, 16, None) \
+        == L.G4_ERR_WORKSPACE
+    assert lib.gemma4_attn_prefill(arr, n, 4, fake, tab, tab, 1, 2048, 2048, fake, None, 1 << 30, None) \
+        == L.G4_ERR_WORKSPACE
+    # non-aliased layer without a value buffer
+    assert lib.gemma4_attn_prefill(arr, n, 4, fake, tab, None, 1, 16, 16, fake, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG
+    # decode: max_kv_len > max_len, NULL kv_len, too many query heads per kv head
+    assert lib.gemma4_attn_decode(arr, n, 4, fake, tab, tab, fake, 4, 100, 200, fake, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG
+    assert lib.gemma4_attn_decode(arr, n, 4, fake, tab, tab, None, 4, 100, 100, fake, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG
+    wide = L.descs([wl.layer_desc(wl.FULL, 512, 32, 1, 1e6, 0, 0)])
+    assert lib.gemma4_attn_decode(wide, 1, 0, fake, tab, tab, fake, 4, 100, 100, fake, fake, 1 << 30, None) \
+        == L.G4_ERR_UNSUPPORTED
+    assert lib.gemma4_attn_decode(arr, n, 4, fake, tab, tab, fake, 64, 8192, 8192, fake, fake, 8, None) \
+        == L.G4_ERR_WORKSPACE
+    # layer index out of range
+    assert lib.gemma4_attn_prefill(arr, n, n, fake, tab, tab, 1, 16, 16, fake, fake, 1 << 20, None) \
+        == L.G4_ERR_INVALID_ARG

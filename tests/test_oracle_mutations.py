@@ -10,20 +10,27 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTATIONS = {
-    "rope_sin_sign": ("y[k] = x0 * c - x1 * s;", "y[k] = x0 * c + x1 * s;"),
-    "rope_dropped_term": ("y[k + half] = x1 * c + x0 * s;", "y[k + half] = x1 * c;"),
-    "rope_exponent": ("double a = pos * pow(theta, -2.0", "double a = pos * pow(theta, -1.0"),
-    "rope_interleaved_pairs": ("double x0 = x[k], x1 = x[k + half];", "double x0 = x[2 * k % D], x1 = x[(2 * k + 1) % D];"),
-    "window_off_by_one": ("if (W > 0 && p - j >= W) return 0;", "if (W > 0 && p - j > W) return 0;"),
-    "causal_off_by_one": ("if (j < 0 || j > p || j >= L) return 0;", "if (j < 0 || j > p + 1 || j >= L) return 0;"),
-    "scale": ("scale = 1.0 / sqrt((double)D);", "scale = 1.0 / (double)D;"),
-    "gqa_prefill_map": ("int64_t kvh = h / g;", "int64_t kvh = h % Hkv;"),
-    "gqa_decode_map": ("int64_t b = r / Hq, h = r % Hq, kvh = h / g;", "int64_t b = r / Hq, h = r % Hq, kvh = h % Hkv;"),
-    "decode_position": ("D, L - 1, L, W, theta", "D, L, L, W, theta"),
-    "values_from_keys": ("const uint16_t* v = vbase + (size_t)j * (size_t)D;",
-                         "const uint16_t* v = kbase + (size_t)j * (size_t)D;"),
+    # name: (anchor, replacement, occurrence to replace; None = every one)
+    "rope_sin_sign": ("y[k] = x0 * c - x1 * s;", "y[k] = x0 * c + x1 * s;", None),
+    "rope_dropped_term": ("y[k + half] = x1 * c + x0 * s;", "y[k + half] = x1 * c;", None),
+    "rope_exponent": ("out[k] = pow(theta, -2.0", "out[k] = pow(theta, -1.0", None),
+    "rope_interleaved_pairs": ("double x0 = x[k], x1 = x[k + half];",
+                               "double x0 = x[2 * k % D], x1 = x[(2 * k + 1) % D];", None),
+    "key_position": ("orc_rope_row_bf16(kbase + (size_t)j * D, D, f, (double)j, tmp, krot + (size_t)j * D);\n    free",
+                     "orc_rope_row_bf16(kbase + (size_t)j * D, D, f, (double)(j + 1), tmp, krot + (size_t)j * D);\n    free",
+                     None),
+    "window_off_by_one": ("if (W > 0 && p - j >= W) return 0;", "if (W > 0 && p - j > W) return 0;", None),
+    "causal_off_by_one": ("if (j < 0 || j > p || j >= L) return 0;", "if (j < 0 || j > p + 1 || j >= L) return 0;",
+                          None),
+    "scale": ("scale = 1.0 / sqrt((double)D);", "scale = 1.0 / (double)D;", None),
+    "gqa_prefill_map": ("if (rb != b || h / g != kvh) continue;", "if (rb != b || h % Hkv != kvh) continue;", 0),
+    "gqa_decode_map": ("if (rb != b || h / g != kvh) continue;", "if (rb != b || h % Hkv != kvh) continue;", 1),
+    "decode_position": ("qpos[nq] = L - 1;", "qpos[nq] = L;", None),
+    "value_row_index": ("const uint16_t* v = vbase + (size_t)j * (size_t)D;",
+                         "const uint16_t* v = vbase + (size_t)(j / 2) * (size_t)D;",
+                         None),
     "softmax_no_max_shift": ("s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);",
-                             "s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m) + 1e-3;"),
+                             "s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m) + 1e-3;", None),
 }
 
 
@@ -31,11 +38,18 @@ MUTATIONS = {
 def test_pins_reject_planted_mistake(name, tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
-    old, new = MUTATIONS[name]
+    old, new, which = MUTATIONS[name]
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
-    assert src.count(old) >= 1, "mutation anchor missing: " + old
+    n = src.count(old)
+    assert n >= 1, "mutation anchor missing: " + old
+    if which is None:
+        out = src.replace(old, new)
+    else:
+        assert which < n
+        parts = src.split(old)
+        out = "".join(p + (new if i == which else old) for i, p in enumerate(parts[:-1])) + parts[-1]
     mutated = tmp_path / "oracle_mut.c"
-    mutated.write_text(src.replace(old, new))
+    mutated.write_text(out)
     lib = tmp_path / "liboracle_mut.so"
     subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(mutated), "-lm"],
                    check=True)
