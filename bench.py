@@ -63,6 +63,10 @@ def time_calls(fn, steps, warmup, flush=None):
     tot_call = tot_kern = 0.0
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for quad in evs:  # torch creates the HIP event on first record; the library re-records k0/k1
+        for e in quad:
+            e.record()
+    torch.cuda.synchronize()
     for i in range(steps):
         if flush is not None:
             flush()
