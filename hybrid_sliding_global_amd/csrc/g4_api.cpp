@@ -144,7 +144,8 @@ G4_EXPORT int gemma4_prefill_workspace_bytes(const g4_layer_desc* layers, int32_
   if (!bytes) return fail(G4_ERR_INVALID_ARG, "bytes is NULL");
   if (batch < 1 || seq_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d", batch, seq_len);
   const g4_layer_desc& d = layers[layer];
-  *bytes = g4::prefill_workspace(batch, seq_len, d.num_kv_heads, d.head_dim);
+  *bytes = g4::prefill_workspace(batch, seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim,
+                                 d.kind == G4_SLIDING ? d.window : 0);
   return ok();
 }
 
@@ -176,7 +177,8 @@ G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers,
   const void* v = d.kv_alias ? k : (v_cache ? v_cache[src] : nullptr);
   if (!k) return fail(G4_ERR_INVALID_ARG, "k_cache[%d] is NULL", src);
   if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
-  const size_t need = g4::prefill_workspace(batch, seq_len, d.num_kv_heads, d.head_dim);
+  const size_t need = g4::prefill_workspace(batch, seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim,
+                                            d.kind == G4_SLIDING ? d.window : 0);
   if (!workspace || workspace_bytes < need)
     return fail(G4_ERR_WORKSPACE, "prefill workspace %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
   g4::PrefillLaunch p;

@@ -20,6 +20,20 @@ void fill_rope_rev(RopeRev* r, int head_dim, double theta);
 // Prefill tiling: key tile size per head size, query rows per work-group.
 constexpr int kPrefillRows = 128;
 inline int prefill_key_tile(int head_dim) { return head_dim == 512 ? 32 : 64; }
+// Waves sharing one 32-row query group (head-dim split) per head size.
+inline int prefill_dsplit(int head_dim) { return head_dim == 512 ? 2 : 1; }
+// Work-groups one prefill launch aims to keep busy: the CU count of an
+// MI355X (one resident prefill work-group per CU).  Fixed so that workspace
+// sizes can be computed without touching the device.
+constexpr int kPrefillSlots = 256;
+
+// How a prefill call is cut into work-groups and how its workspace is laid
+// out: [rotated key tiles][arrival counters][partial-result slots].
+struct PrefillPlan {
+  int BN = 0, ntiles = 0, g = 0, nqt = 0, npair = 0, kpieces = 0;
+  size_t kimg_bytes = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0, total = 0;
+};
+PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W);
 
 struct PrefillLaunch {
   const void* q;      // bf16 [B, S, Hq, D]
@@ -38,7 +52,7 @@ struct ProfileEvents {
   hipEvent_t after = nullptr;
 };
 
-size_t prefill_workspace(int B, int S, int Hkv, int D);
+size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const ProfileEvents& ev);
 
 // Decode split-K planning: keys per work-group and number of chunks.

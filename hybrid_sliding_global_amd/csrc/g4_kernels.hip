@@ -50,7 +50,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // log2 units
-constexpr int kFragBatch = 4;         // LDS operand fragments in flight per MFMA batch
+constexpr int kDecodeStages = 4;      // 16-row key/value stages in the decode LDS ring (2 when K and V
+                                      // are both staged at head size 512, so two work-groups share a CU)
 
 // ---------------------------------------------------------------- helpers --
 
@@ -219,11 +220,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Rotate raw keys rows [0, S) of one (batch, kv-head) slice into the tile
 // image: tile t holds rows t*BN .. t*BN+BN-1, each row's 16-byte chunks at
-// swizzled positions; rows >= S are zero.
+// swizzled positions; rows >= S are zero.  Also clears the attention
+// kernel's arrival counters (this launch precedes it on the same stream).
 template <int D, int BN>
 __global__ __launch_bounds__(256) void k_rope_keys(const uint16_t* __restrict__ k, uint16_t* __restrict__ img, int S,
-                                                   int Hkv, int Lmax, int ntiles, RopeRev rope) {
+                                                   int Hkv, int Lmax, int ntiles, RopeRev rope, int* counters,
+                                                   int ncounters) {
   const int t = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int flat = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+  for (int i = flat * 256 + threadIdx.x; i < ncounters; i += gridDim.x * gridDim.y * gridDim.z * 256) counters[i] = 0;
   const uint16_t* src = k + ((size_t)b * Hkv + kvh) * (size_t)Lmax * D;
   uint16_t* dst = img + (((size_t)b * Hkv + kvh) * ntiles + t) * (size_t)(BN * D);
   constexpr int CH = D / 16;  // chunk c pairs with chunk c + CH
@@ -249,19 +254,37 @@ struct PrefillArgs {
   const uint16_t* kimg;
   const uint16_t* v;
   float* out;
-  int B, S, Hq, Hkv, g, Lmax, W, ntiles, nqt;
+  int* counters;  // [B * Hkv * nqt] arrival counts (zeroed by the key pass)
+  float* part;    // partial-result slots
+  int B, S, Hq, Hkv, g, Lmax, W, ntiles, nqt, npair, kpieces;
   float qscale;  // softmax scale * log2(e): scores come out in log2 units
   RopeRev rope;
 };
 
-// DS = number of waves sharing one 32-row query group, each owning 1/DS of
-// the head dimension (DS = 2 for head size 512 keeps the 32 x 512 fp32
-// output block of a row group in two waves' accumulators).  The work-group
-// is 4 * DS waves and covers 128 query rows.
+__device__ __forceinline__ float max_lane_pair(float x) {  // max over lanes l and l ^ 32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Flash-style prefill.  DS = number of waves sharing one 32-row query group,
+// each owning 1/DS of the head dimension (DS = 2 for head size 512 keeps
+// the 32 x 512 fp32 output block of a row group in two waves'
+// accumulators).  A work-group is 4 * DS waves and covers one 128-row query
+// tile of one (batch, kv-head) at a time.
+//
+// Work split: the query tiles of a (batch, kv-head) are paired long with
+// short (t with nqt-1-t), so a pair's key-tile count is nearly the same for
+// every pair, and each pair's concatenated key work is cut into kpieces
+// equal ranges, one per work-group.  A query tile cut across work-groups is
+// finished by whichever of its pieces arrives last: every piece stores its
+// partial (O, running max, running sum) and bumps the tile's counter; the
+// last one merges the others into its own registers and writes the output.
+// Nobody waits for anybody.
 template <int D, int BN, int DS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256 * DS, 256 * DS), amdgpu_waves_per_eu(DS, DS))) void
 k_prefill(PrefillArgs a) {
   constexpr int NT = 256 * DS;                // threads
+  constexpr int NW = 4 * DS;                  // waves
   constexpr int KSTEPS = D / 16;              // 32x32x16 steps over the head dim
   constexpr int KSW = KSTEPS / DS;            // steps owned by one wave
   constexpr int MB = BN / 32;                 // 32-key blocks per tile
@@ -269,71 +292,65 @@ k_prefill(PrefillArgs a) {
   constexpr int DBW = DB / DS;                // output blocks owned by one wave
   constexpr int LPT = BN * D * 2 / (NT * 16); // 16-byte loads per thread per tile and tensor
   constexpr int ROWB = D * 2;
+  constexpr int ACC_F4 = NW * DBW * 4 * 64;   // f32x4 per partial slot (accumulators)
   static_assert(LPT * NT * 16 == BN * D * 2, "tile must split evenly over the threads");
 
   // Double-buffered key / value tiles.  The two buffers are distinct objects
   // and the tile loop is unrolled by two, so the compiler can tell that the
-  // direct-to-LDS prefetch of the next tile never aliases the tile being read
-  // and does not drain it before the first LDS read.
+  // direct-to-LDS prefetch of the next tile never aliases the tile being read.
   __shared__ __attribute__((aligned(16))) uint16_t sk0[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sk1[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sv0[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sv1[BN * D];
-  __shared__ f32x16 sx[DS > 1 ? 4 * DS : 1][MB][64];  // partial S^T exchange
+  __shared__ f32x16 sx[DS > 1 ? NW : 1][MB][64];  // partial S^T exchange
+  // The arrival flag of a split tile lives in the first word of a key
+  // buffer: no tile is in flight when it is written and read.
+  int* s_last = reinterpret_cast<int*>(sk0);
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lives in SGPRs
   const int rg = wave / DS, dp = wave % DS;
-  const int nbh = a.B * a.Hkv;
-  const int bh = blockIdx.x % nbh;
-  const int qt = a.nqt - 1 - (int)(blockIdx.x / nbh);  // longest query tiles first
+
+  // Work id: consecutive ids (same batch / kv-head) go to the same XCD, whose
+  // L2 then serves their shared key/value tiles.
+  const int nblk = gridDim.x;
+  const int wid = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int per_bh = a.npair * a.kpieces;
+  const int bh = wid / per_bh, rem = wid % per_bh, pair = rem / a.kpieces, piece = rem % a.kpieces;
   const int kvh = bh % a.Hkv, b = bh / a.Hkv;
   const int rows_total = a.S * a.g;
-  const int r0 = qt * 128;
-  const int r = r0 + rg * 32 + n;
-  const bool valid = r < rows_total;
-  const int rc = valid ? r : rows_total - 1;
-  const int pos = rc / a.g, head = kvh * a.g + rc % a.g;
-  const int pos_min = r0 / a.g;
-  const int pos_max = min(r0 + 127, rows_total - 1) / a.g;
+  const bool windowed = a.W > 0;
 
-  // Q' = RoPE(q) * scale * log2(e), as the B operand of S^T = K' Q'^T:
-  // lane (n, h) holds head-dim elements 16*ks + 8*h + [0, 8) of its query
-  // row for the k-steps this wave owns.  Rotation partners (d, d + D/2) sit
-  // in k-steps ks and ks + KSTEPS/2: with DS = 2 the first half of each
-  // wave's steps pairs with the second.
-  bf16x8 qf[KSW];
-  {
-    const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
-#pragma unroll
-    for (int i = 0; i < KSW / 2; ++i) {
-      const int ks = dp * (KSW / 2) + i;  // first-half step, partner ks + KSTEPS/2
-      const int d0 = 16 * ks + 8 * h;
-      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
-      u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
-      rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
-      qf[i] = as_bf16x8(x);
-      qf[i + KSW / 2] = as_bf16x8(y);
-    }
-  }
+  auto tile_keys = [&](int qt, int& jlo, int& jhi) {
+    const int r0 = qt * 128;
+    const int pmin = r0 / a.g, pmax = min(r0 + 127, rows_total - 1) / a.g;
+    jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
+    jhi = pmax / BN;
+  };
+  const int tl = a.nqt - 1 - pair;       // long tile of the pair
+  const int ts = pair < tl ? pair : -1;  // short tile (none for the middle of an odd count)
+  int jlo_l, jhi_l, jlo_s = 0, jhi_s = -1;
+  tile_keys(tl, jlo_l, jhi_l);
+  if (ts >= 0) tile_keys(ts, jlo_s, jhi_s);
+  const int nL = jhi_l - jlo_l + 1, nS = ts >= 0 ? jhi_s - jlo_s + 1 : 0, U = nL + nS;
+  auto ubound = [&](int j) { return (int)(((long long)j * U) / a.kpieces); };
+  const int u0 = ubound(piece), u1 = ubound(piece + 1);
 
   const uint16_t* kimg = a.kimg + (size_t)(b * a.Hkv + kvh) * a.ntiles * (size_t)(BN * D);
   const uint16_t* vsl = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
-  const int key_lo = a.W > 0 ? max(0, pos_min - a.W + 1) : 0;
-  const int j_lo = key_lo / BN, j_hi = pos_max / BN;
 
   auto issue = [&](int j, uint16_t* dk, uint16_t* dv) {
-    int ln = lane;  // opaque: keep the per-lane address math inside the loop (see below)
+    int ln = lane;  // opaque: keep the per-lane address math inside the loop
     asm volatile("" : "+v"(ln));
     const char* ksrc = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int blk = i * (NT / 64) + wave;
+      const int blk = i * NW + wave;
       g2l16(ksrc + blk * 1024 + ln * 16, reinterpret_cast<char*>(dk) + blk * 1024);
     }
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int blk = i * (NT / 64) + wave;
+      const int blk = i * NW + wave;
       const int byte = blk * 1024 + ln * 16;
       const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
       const int src_row = min(j * BN + row, a.S - 1);  // rows past the sequence: any valid row, weight 0
@@ -341,157 +358,250 @@ k_prefill(PrefillArgs a) {
     }
   };
 
-  f32x16 acc[DBW];
-#pragma unroll
-  for (int i = 0; i < DBW; ++i) acc[i] = f32x16{};
-  float m_i = kNegInf, l_i = 0.f;
+  // One segment: query tile qt against key tiles [jb, je]; seg = 0 (long) or 1 (short).
+  auto process = [&](int qt, int seg, int jb, int je, int jlo_t, int jhi_t, int us, int ue) {
+    const int r0 = qt * 128;
+    const int r = r0 + rg * 32 + n;
+    const bool valid = r < rows_total;
+    const int rc = valid ? r : rows_total - 1;
+    const int pos = rc / a.g, head = kvh * a.g + rc % a.g;
+    const int pos_min = r0 / a.g;
+    const int pos_max = min(r0 + 127, rows_total - 1) / a.g;
 
-  const bool windowed = a.W > 0;
-
-  auto step = [&](int j, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
-    if (j < j_hi) {
-      issue(j + 1, nk, nv);
-      wait_vm<2 * LPT>();
-    } else {
-      wait_vm<0>();
-    }
-    lds_barrier();
-
-    // Per-lane LDS offsets are recomputed every tile from an opaque copy of
-    // the lane index instead of being hoisted out of the loop, which would pin
-    // a few dozen registers for the whole kernel.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int on = ln & 31, oh = ln >> 5, oG = ln >> 4, oi16 = ln & 15;
-
-    // S^T = K' Q'^T for this tile: s[mb] holds keys 32*mb + 8*i + 4*h + jj (reg 4*i + jj) of query n.
-    f32x16 s[MB];
-    const char* kb = reinterpret_cast<const char*>(ck);
+    // Q' = RoPE(q) * scale * log2(e), as the B operand of S^T = K' Q'^T:
+    // lane (n, h) holds head-dim elements 16*ks + 8*h + [0, 8) of its query
+    // row for the k-steps this wave owns.  Rotation partners (d, d + D/2)
+    // sit in k-steps ks and ks + KSTEPS/2.
+    bf16x8 qf[KSW];
+    {
+      const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      s[mb] = f32x16{};
-      const int row = 32 * mb + on;
-      const char* kr = kb + row * ROWB;
-      const int sw = swz(row);
-      const unsigned kra = lds_addr(kr);
-#pragma unroll
-      for (int i0 = 0; i0 < KSW; i0 += 4) {
-        unsigned ad[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u;
-          const int ks = i < KSW / 2 ? dp * (KSW / 2) + i : KSTEPS / 2 + dp * (KSW / 2) + (i - KSW / 2);
-          ad[u] = kra + (((2 * ks + oh) ^ sw) << 4);
-        }
-        u32x4 kf[4];
-        lds_read_b128x4(kf, ad);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s[mb] = mfma32(as_bf16x8(kf[u]), qf[i0 + u], s[mb]);
+      for (int i = 0; i < KSW / 2; ++i) {
+        const int ks = dp * (KSW / 2) + i;  // first-half step, partner ks + KSTEPS/2
+        const int d0 = 16 * ks + 8 * h;
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+        u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+        rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
+        qf[i] = as_bf16x8(x);
+        qf[i + KSW / 2] = as_bf16x8(y);
       }
     }
-    if constexpr (DS > 1) {
-      // exchange the two halves of the head-dim sum within the wave pair;
-      // float addition is commutative, so both waves get identical scores
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) lds_write_f32x16(lds_addr(&sx[wave][mb][ln]), s[mb]);
-      lds_barrier();
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) s[mb] += lds_read_f32x16(lds_addr(&sx[wave ^ 1][mb][ln]));
-    }
 
-    const int kbase = j * BN;
-    const bool need_mask = (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
-    if (need_mask) {
+    f32x16 acc[DBW];
+#pragma unroll
+    for (int i = 0; i < DBW; ++i) acc[i] = f32x16{};
+    float m_i = kNegInf, l_i = 0.f;
+
+    auto step = [&](int j, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
+      wait_vm<0>();  // this wave's share of tile j has landed
+      lds_barrier();  // everybody's share has, and tile j-1 is no longer being read
+      if (j < je) issue(j + 1, nk, nv);
+
+      // Per-lane LDS offsets are recomputed every tile from an opaque copy of
+      // the lane index instead of being hoisted out of the loop, which would
+      // pin a few dozen registers for the whole kernel.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int on = ln & 31, oh = ln >> 5, oG = ln >> 4, oi16 = ln & 15;
+
+      // S^T = K' Q'^T for this tile: s[mb] holds keys 32*mb + 8*i + 4*h + jj (reg 4*i + jj) of query n.
+      f32x16 s[MB];
+      const char* kb = reinterpret_cast<const char*>(ck);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s[mb] = f32x16{};
+        const int row = 32 * mb + on;
+        const int sw = swz(row);
+        const unsigned kra = lds_addr(kb + row * ROWB);
+#pragma unroll
+        for (int i0 = 0; i0 < KSW; i0 += 4) {
+          unsigned ad[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u;
+            const int ks = i < KSW / 2 ? dp * (KSW / 2) + i : KSTEPS / 2 + dp * (KSW / 2) + (i - KSW / 2);
+            ad[u] = kra + (((2 * ks + oh) ^ sw) << 4);
+          }
+          u32x4 kf[4];
+          lds_read_b128x4(kf, ad);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) s[mb] = mfma32(as_bf16x8(kf[u]), qf[i0 + u], s[mb]);
+        }
+      }
+      if constexpr (DS > 1) {
+        // exchange the two halves of the head-dim sum within the wave pair;
+        // float addition is commutative, so both waves get identical scores
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) lds_write_f32x16(lds_addr(&sx[wave][mb][ln]), s[mb]);
+        lds_barrier();
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) s[mb] += lds_read_f32x16(lds_addr(&sx[wave ^ 1][mb][ln]));
+      }
+
+      const int kbase = j * BN;
+      const bool need_mask = (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
+      if (need_mask) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
+            const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+            s[mb][rr] = vis ? s[mb][rr] : kNegInf;
+          }
+      }
+
+      // Online softmax in the log2 domain; lanes n and n+32 share query n.
+      // The reference maximum m_i only moves when a score exceeds it by more
+      // than kRescaleSlack, so P = 2^(s - m_i) <= 2^kRescaleSlack and the
+      // MFMA accumulators are rescaled only on those (rare) tiles.
+      float mx = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
-          const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
-          s[mb][rr] = vis ? s[mb][rr] : kNegInf;
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+      mx = max_lane_pair(mx);
+      const bool grow = mx > m_i + kRescaleSlack;
+      // lanes with m_i = -inf have nothing accumulated yet: they just adopt mx
+      const float alpha = (grow & (m_i != kNegInf)) ? fast_exp2(m_i - mx) : 1.f;
+      m_i = grow ? mx : m_i;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        l_i *= alpha;
+#pragma unroll
+        for (int i = 0; i < DBW; ++i) acc[i] *= alpha;
+      }
+      const float m_use = (m_i == kNegInf) ? 0.f : m_i;
+      float rs = 0.f;
+      unsigned pk[MB * 8];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) {
+          const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
+          rs += p0 + p1;
+          pk[mb * 8 + rr / 2] = pack_bf16(p0, p1);
         }
+      l_i += rs;
+
+      // O^T += V^T P^T.  P^T slot t of key-step ks is key 16*ks + 4*hh + t (t < 4)
+      // or 16*ks + 8 + 4*hh + (t - 4); the transpose reads fetch V in that order.
+      const char* vb = reinterpret_cast<const char*>(cv);
+      const int ohh = oG >> 1, odsub = 16 * (oG & 1);
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks) {
+        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+        const int row1 = 16 * ks + 4 * ohh + (oi16 >> 2), row2 = row1 + 8;
+        const unsigned v1 = lds_addr(vb + row1 * ROWB), v2 = lds_addr(vb + row2 * ROWB);
+        const int sw1 = swz(row1), sw2 = swz(row2);
+#pragma unroll
+        for (int i0 = 0; i0 < DBW; i0 += 4) {
+          unsigned ad[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int dcol = 32 * (dp * DBW + i0 + u) + odsub + 4 * (oi16 & 3);
+            const int chunk = dcol >> 3, half = (dcol & 7) << 1;
+            ad[2 * u] = v1 + ((chunk ^ sw1) << 4) + half;
+            ad[2 * u + 1] = v2 + ((chunk ^ sw2) << 4) + half;
+          }
+          u32x2 t[8];
+          lds_read_tr_x8(t, ad);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[i0 + u] = mfma32(cat2(t[2 * u], t[2 * u + 1]), pf, acc[i0 + u]);
+        }
+      }
+    };
+
+    issue(jb, sk0, sv0);
+    for (int j = jb;;) {
+      step(j, sk0, sv0, sk1, sv1);
+      if (++j > je) break;
+      step(j, sk1, sv1, sk0, sv0);
+      if (++j > je) break;
     }
 
-    // Online softmax in the log2 domain; lanes n and n+32 share query n.  The
-    // reference maximum m_i only moves when a score exceeds it by more than
-    // kRescaleSlack, so P = 2^(s - m_i) <= 2^kRescaleSlack and the MFMA
-    // accumulators are rescaled only on those (rare) tiles.
-    float mx = kNegInf;
+    if (jb != jlo_t || je != jhi_t) {
+      // Partial: store (O, m, l), then count this piece in.
+      const size_t slot_f4 = (size_t)ACC_F4 + NW * 64 / 2;  // f32x4 units per slot (m and l: NW*64 floats each)
+      auto slot_ptr = [&](int pc) {
+        return reinterpret_cast<f32x4*>(a.part) + (((size_t)bh * a.npair + pair) * a.kpieces + pc) * 2 * slot_f4 +
+               (size_t)seg * slot_f4;
+      };
+      f32x4* mine = slot_ptr(piece);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int db = 0; db < DBW; ++db)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = mx > m_i + kRescaleSlack;
-    // lanes with m_i = -inf have nothing accumulated yet: they just adopt mx
-    const float alpha = (grow & (m_i != kNegInf)) ? fast_exp2(m_i - mx) : 1.f;
-    m_i = grow ? mx : m_i;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-      l_i *= alpha;
-#pragma unroll
-      for (int i = 0; i < DBW; ++i) acc[i] *= alpha;
-    }
-    const float m_use = (m_i == kNegInf) ? 0.f : m_i;
-    float rs = 0.f;
-    unsigned pk[MB * 8];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
-        rs += p0 + p1;
-        pk[mb * 8 + rr / 2] = pack_bf16(p0, p1);
+        for (int qd = 0; qd < 4; ++qd)
+          mine[((wave * DBW + db) * 4 + qd) * 64 + lane] =
+              f32x4{acc[db][4 * qd], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
+      float* ml = reinterpret_cast<float*>(mine + ACC_F4);
+      ml[wave * 64 + lane] = m_i;
+      ml[NW * 64 + wave * 64 + lane] = l_i;
+      __threadfence();
+      __syncthreads();
+      int npieces = 0;
+      for (int pc = 0; pc < a.kpieces; ++pc) {
+        const int x0 = ubound(pc), x1 = ubound(pc + 1);
+        npieces += (x0 < x1 && x0 < ue && x1 > us) ? 1 : 0;
       }
-    l_i += rs;
+      if (tid == 0) *s_last = atomicAdd(&a.counters[(size_t)bh * a.nqt + qt], 1) == npieces - 1;
+      __syncthreads();
+      const bool last = *s_last != 0;
+      __syncthreads();  // the buffer is refilled by the next segment
+      if (!last) return;
+      __threadfence();
+      // Deterministic merge: the result must not depend on which piece came
+      // last, so every piece (this one re-read from its own slot) is added in
+      // ascending piece order against the common maximum of all pieces.
+      auto is_piece = [&](int pc) {
+        const int x0 = ubound(pc), x1 = ubound(pc + 1);
+        return x0 < x1 && x0 < ue && x1 > us;
+      };
+      float M = kNegInf;
+      for (int pc = 0; pc < a.kpieces; ++pc)
+        if (is_piece(pc)) M = fmaxf(M, reinterpret_cast<const float*>(slot_ptr(pc) + ACC_F4)[wave * 64 + lane]);
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) acc[db] = f32x16{};
+      l_i = 0.f;
+      for (int pc = 0; pc < a.kpieces; ++pc) {
+        if (!is_piece(pc)) continue;
+        const f32x4* src = slot_ptr(pc);
+        const float* sml = reinterpret_cast<const float*>(src + ACC_F4);
+        const float mp = sml[wave * 64 + lane], lp = sml[NW * 64 + wave * 64 + lane];
+        const float f = mp == kNegInf ? 0.f : fast_exp2(mp - M);
+        l_i += lp * f;
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 o = src[((wave * DBW + db) * 4 + qd) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * qd + e] += o[e] * f;
+          }
+      }
+      m_i = M;
+    }
 
-    // O^T += V^T P^T.  P^T slot t of key-step ks is key 16*ks + 4*hh + t (t < 4)
-    // or 16*ks + 8 + 4*hh + (t - 4); the transpose reads fetch V in that order.
-    const char* vb = reinterpret_cast<const char*>(cv);
-    const int ohh = oG >> 1, odsub = 16 * (oG & 1);
+    const float l = l_i + __shfl_xor(l_i, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (valid) {
+      float* orow = a.out + (((size_t)b * a.S + pos) * a.Hq + head) * D + 32 * dp * DBW;
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const bf16x8 pf = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
-      const int row1 = 16 * ks + 4 * ohh + (oi16 >> 2), row2 = row1 + 8;
-      const unsigned v1 = lds_addr(vb + row1 * ROWB), v2 = lds_addr(vb + row2 * ROWB);
-      const int sw1 = swz(row1), sw2 = swz(row2);
+      for (int db = 0; db < DBW; ++db)
 #pragma unroll
-      for (int i0 = 0; i0 < DBW; i0 += 4) {
-        unsigned ad[8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int dcol = 32 * (dp * DBW + i0 + u) + odsub + 4 * (oi16 & 3);
-          const int chunk = dcol >> 3, half = (dcol & 7) << 1;
-          ad[2 * u] = v1 + ((chunk ^ sw1) << 4) + half;
-          ad[2 * u + 1] = v2 + ((chunk ^ sw2) << 4) + half;
+        for (int i = 0; i < 4; ++i) {
+          f32x4 o = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv,
+                     acc[db][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * h) = o;
         }
-        u32x2 t[8];
-        lds_read_tr_x8(t, ad);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[i0 + u] = mfma32(cat2(t[2 * u], t[2 * u + 1]), pf, acc[i0 + u]);
-      }
     }
-    lds_barrier();
   };
 
-  issue(j_lo, sk0, sv0);
-  for (int j = j_lo;;) {
-    step(j, sk0, sv0, sk1, sv1);
-    if (++j > j_hi) break;
-    step(j, sk1, sv1, sk0, sv0);
-    if (++j > j_hi) break;
-  }
-
-  const float l = l_i + __shfl_xor(l_i, 32);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (valid) {
-    float* orow = a.out + (((size_t)b * a.S + pos) * a.Hq + head) * D + 32 * dp * DBW;
-#pragma unroll
-    for (int db = 0; db < DBW; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 o = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * h) = o;
-      }
+  if (u0 < u1) {
+    if (u0 < nL) process(tl, 0, jlo_l + u0, jlo_l + min(u1, nL) - 1, jlo_l, jhi_l, 0, nL);
+    if (u1 > nL) {
+      if (u0 < nL) lds_barrier();  // the first segment's last tile may still be in use
+      process(ts, 1, jlo_s + max(u0, nL) - nL, jlo_s + u1 - nL - 1, jlo_s, jhi_s, nL, U);
+    }
   }
 }
 
@@ -509,20 +619,87 @@ struct DecodeArgs {
   RopeRev rope;
 };
 
+// Rotate 8 (x, y) pairs held as packed bf16 quads by per-pair (cos, sin)
+// constants cs[2e], cs[2e+1] for e = 0..7 (pair e = element e of x and y).
+__device__ __forceinline__ void rot8_const(u32x4& x, u32x4& y, const float* cs) {
+  u32x4 xo, yo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float c0 = cs[4 * e], s0 = cs[4 * e + 1], c1 = cs[4 * e + 2], s1 = cs[4 * e + 3];
+    const float a0 = bf_lo(x[e]), a1 = bf_hi(x[e]);
+    const float b0 = bf_lo(y[e]), b1 = bf_hi(y[e]);
+    xo[e] = pack_bf16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+    yo[e] = pack_bf16(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+  }
+  x = xo;
+  y = yo;
+}
+
+__device__ __forceinline__ void lds_read_b128x2(u32x4 (&r)[2], const unsigned (&ad)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(ad[0]), "v"(ad[1]));
+}
+
+__device__ __forceinline__ void lds_read_tr_x4(u32x2 (&r)[4], const unsigned (&ad)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
+}
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+__device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b), c, 0,
+                                                   0, 0);
+}
+
+// max over the four 16-lane groups that share a query column
+__device__ __forceinline__ float max_over_groups(float x) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Split-K decode.  Scores need <R_P q, R_j k> (P = kv_len - 1, j = key
+// position); RoPE rotations are orthogonal and commute, so this equals
+// <R_{P - j0} q, R_{j - j0} k> for any j0.  With j0 = the first key of the
+// current 16-key step, every lane's key offset j - j0 (its MFMA row) and its
+// rotation pairs are fixed for the whole work-group: their (cos, sin) are
+// computed once, and the query is advanced by R_{-16} once per step (fp32
+// recurrence).  The four waves split the rotation pairs for S^T = K' Q'^T
+// (partial sums exchanged through LDS) and the head dim for O^T += V^T P^T.
+// Key/value rows stream through NSTAGE LDS stages of 16 rows each.
 template <int D, bool ALIAS, int NSTAGE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(DecodeArgs a) {
-  constexpr int KPS = 32;            // keys per step
+  constexpr int KPS = 16;            // keys per step
   constexpr int FQ = D / 8;          // rotation pairs per wave
-  constexpr int KSTEPS = FQ / 16;    // 16x16x32 steps per key block (both halves of each pair)
+  constexpr int KH = FQ / 32;        // groups of 8 pairs per lane (x and y halves each)
+  constexpr int KSTEPS = 2 * KH;     // 16x16x32 steps per key block
   constexpr int DQ = D / 4;          // output head-dim slice per wave
   constexpr int DBLK = DQ / 16;
   constexpr int NT = ALIAS ? 1 : 2;  // tensors staged per step
   constexpr int ROWB = D * 2;
   constexpr int LPS1 = KPS * ROWB / 4096;
   constexpr int LPS = NT * LPS1;
+  static_assert(LPS1 >= 1 && LPS1 * 4096 == KPS * ROWB, "stage must split over 256 threads");
 
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[NSTAGE][NT][KPS * D];
-  __shared__ f32x4 red[4][2][64];
+  __shared__ f32x4 red[4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, G = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -542,24 +719,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
     return;
   }
 
-  // Q' of this wave's rotation pairs, as the B operand (N = query heads).
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + head) * D;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS / 2; ++kk) {
-      const int d0 = wave * FQ + 32 * kk + 8 * G;
-      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
-      u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
-      rope8(x, y, a.rope.rev, d0, (double)(L - 1), a.qscale);
-      if (!qvalid) x = y = u32x4{0, 0, 0, 0};
-      qf[kk] = as_bf16x8(x);
-      qf[kk + KSTEPS / 2] = as_bf16x8(y);
-    }
-  }
-
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   auto issue = [&](int step, int stg) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     const int k0 = k_start + step * KPS;
 #pragma unroll
     for (int tsr = 0; tsr < NT; ++tsr) {
@@ -567,7 +730,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 #pragma unroll
       for (int i = 0; i < LPS1; ++i) {
         const int blk = i * 4 + wave;
-        const int byte = blk * 1024 + lane * 16;
+        const int byte = blk * 1024 + ln * 16;
         const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
         const int src_row = min(k0 + row, k_end - 1);
         g2l16(base + (size_t)src_row * D + ((slot ^ swz(row)) << 3),
@@ -576,18 +739,80 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
     }
   };
 
-  f32x4 acc[DBLK];
-#pragma unroll
-  for (int i = 0; i < DBLK; ++i) acc[i] = f32x4{};
-  float m_i = kNegInf, l_i = 0.f;
-
+  // Start streaming before the per-lane set-up below.
   const int nsteps = (k_end - k_start + KPS - 1) / KPS;
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nsteps) issue(s, s);
 
+  // This lane's rotation pairs: f = wave*FQ + 32*kk + 8*G + t (kk < KH, t < 8).
+  // Key side: (cos, sin)(n * w_f) for its key offset n < 16 (fp32 is exact
+  // enough for angles below 16 rad).
+  float kcs[KH][16];
+#pragma unroll
+  for (int kk = 0; kk < KH; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int f = wave * FQ + 32 * kk + 8 * G + t;
+      float x = (float)n * (float)a.rope.rev[f];
+      x -= __builtin_rintf(x);
+      kcs[kk][2 * t] = __builtin_amdgcn_cosf(x);
+      kcs[kk][2 * t + 1] = __builtin_amdgcn_sinf(x);
+    }
+  // Query side: u = RoPE(q, P - k_start) * scale * log2(e) in fp32 (fp64
+  // angle), and the per-step rotation R_{-16}.
+  float ux[KH][8], uy[KH][8], stc[KH][8], sts[KH][8];
+  {
+    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + head) * D;
+    const double rel = (double)(L - 1 - k_start);
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      const int d0 = wave * FQ + 32 * kk + 8 * G;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float sn, cn;
+        sincos_rev(rel, a.rope.rev[d0 + t], sn, cn);
+        float st = (float)KPS * (float)a.rope.rev[d0 + t];
+        st -= __builtin_rintf(st);
+        const float xa = (t & 1) ? bf_hi(x[t >> 1]) : bf_lo(x[t >> 1]);
+        const float ya = (t & 1) ? bf_hi(y[t >> 1]) : bf_lo(y[t >> 1]);
+        ux[kk][t] = qvalid ? (xa * cn - ya * sn) * a.qscale : 0.f;
+        uy[kk][t] = qvalid ? (ya * cn + xa * sn) * a.qscale : 0.f;
+        stc[kk][t] = __builtin_amdgcn_cosf(st);
+        sts[kk][t] = -__builtin_amdgcn_sinf(st);  // rotation by -KPS positions
+      }
+    }
+  }
+
+  f32x4 acc[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) acc[i] = f32x4{};
+  float m_i = kNegInf, l_i = 0.f;
+
   for (int s = 0; s < nsteps; ++s) {
     const int stg = s % NSTAGE;
+    // Q' for this step (bf16), then advance u by R_{-16} for the next one.
+    bf16x8 qf[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      u32x4 x, y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = pack_bf16(ux[kk][2 * e], ux[kk][2 * e + 1]);
+        y[e] = pack_bf16(uy[kk][2 * e], uy[kk][2 * e + 1]);
+      }
+      qf[kk] = as_bf16x8(x);
+      qf[kk + KH] = as_bf16x8(y);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float xa = ux[kk][t], ya = uy[kk][t];
+        ux[kk][t] = xa * stc[kk][t] - ya * sts[kk][t];
+        uy[kk][t] = ya * stc[kk][t] + xa * sts[kk][t];
+      }
+    }
+
     if (nsteps - s - 1 >= NSTAGE - 2)
       wait_vm<(NSTAGE - 2) * LPS>();
     else
@@ -600,99 +825,81 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
     const int on = ln & 15, oG = ln >> 4;
     const int k0 = k_start + s * KPS;
     const char* kb = reinterpret_cast<const char*>(sbuf[stg][0]);
-    // Partial S^T over this wave's rotation pairs; keys rotated on the fly.
-    // Fragment e of the batch: key block mb = e / (KSTEPS) ..., x/y halves.
-    constexpr int NFR = 2 * KSTEPS;  // 16-byte fragments per step and lane (x and y, both key blocks)
-    static_assert(NFR % 4 == 0, "fragment batches of four");
-    f32x4 sp[2] = {f32x4{}, f32x4{}};
+    // Partial S^T over this wave's rotation pairs; lane (n, G) supplies key
+    // row n, rotated by its offset n within the step.
+    f32x4 sp = f32x4{};
+    const unsigned kra = lds_addr(kb + on * ROWB);
+    const int ksw = swz(on);
 #pragma unroll
-    for (int e0 = 0; e0 < NFR; e0 += 4) {
+    for (int kk = 0; kk < KH; ++kk) {
+      const int d = wave * FQ + 32 * kk + 8 * oG;
+      const unsigned ad[2] = {kra + (((d >> 3) ^ ksw) << 4), kra + ((((d + D / 2) >> 3) ^ ksw) << 4)};
+      u32x4 fr[2];
+      lds_read_b128x2(fr, ad);
+      rot8_const(fr[0], fr[1], kcs[kk]);
+      sp = mfma16(as_bf16x8(fr[0]), qf[kk], sp);
+      sp = mfma16(as_bf16x8(fr[1]), qf[kk + KH], sp);
+    }
+    lds_write_f32x4(lds_addr(&red[wave][ln]), sp);
+    lds_barrier();
+    f32x4 sc;
+    {
+      u32x4 t[4];
+      const unsigned ad[4] = {lds_addr(&red[0][ln]), lds_addr(&red[1][ln]), lds_addr(&red[2][ln]),
+                              lds_addr(&red[3][ln])};
+      lds_read_b128x4(t, ad);
+      sc = __builtin_bit_cast(f32x4, t[0]) + __builtin_bit_cast(f32x4, t[1]) + __builtin_bit_cast(f32x4, t[2]) +
+           __builtin_bit_cast(f32x4, t[3]);
+    }
+
+    // keys k0 + 4*G + jj for query n
+    float mx = kNegInf;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int key = k0 + 4 * G + jj;
+      sc[jj] = key < k_end ? sc[jj] : kNegInf;
+      mx = fmaxf(mx, sc[jj]);
+    }
+    mx = max_over_groups(mx);
+    const bool grow = mx > m_i + kRescaleSlack;
+    const float alpha = (grow & (m_i != kNegInf)) ? fast_exp2(m_i - mx) : 1.f;
+    m_i = grow ? mx : m_i;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      l_i *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) acc[i] *= alpha;
+    }
+    const float m_use = (m_i == kNegInf) ? 0.f : m_i;
+    float p[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      p[jj] = fast_exp2(sc[jj] - m_use);
+      l_i += p[jj];
+    }
+    const u32x2 pf = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+
+    // O^T += V^T P^T with 16x16x16 MFMAs: P^T slot t of lane group G is key
+    // 4*G + t, which one transpose read per output block fetches.
+    const char* vb = reinterpret_cast<const char*>(sbuf[stg][NT - 1]);
+    const int vrow = 4 * oG + (on >> 2);
+    const unsigned va = lds_addr(vb + vrow * ROWB);
+    const int vsw = swz(vrow);
+#pragma unroll
+    for (int b0 = 0; b0 < DBLK; b0 += 4) {
       unsigned ad[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u, mb = e / KSTEPS, kk = (e % KSTEPS) / 2, hi = e & 1;
-        const int row = 16 * mb + on;
-        const int d = wave * FQ + 32 * kk + 8 * oG + (hi ? D / 2 : 0);
-        ad[u] = lds_addr(kb + row * ROWB) + (((d >> 3) ^ swz(row)) << 4);
-      }
-      u32x4 fr[4];
-      lds_read_b128x4(fr, ad);
-#pragma unroll
-      for (int u = 0; u < 4; u += 2) {
-        const int e = e0 + u, mb = e / KSTEPS, kk = (e % KSTEPS) / 2;
-        const int d0 = wave * FQ + 32 * kk + 8 * G;
-        u32x4 x = fr[u], y = fr[u + 1];
-        rope8(x, y, a.rope.rev, d0, (double)(k0 + 16 * mb + n), 1.0f);
-        sp[mb] = mfma16(as_bf16x8(x), qf[kk], sp[mb]);
-        sp[mb] = mfma16(as_bf16x8(y), qf[kk + KSTEPS / 2], sp[mb]);
-      }
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) lds_write_f32x4(lds_addr(&red[wave][mb][ln]), sp[mb]);
-    lds_barrier();
-    f32x4 sc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      u32x4 t[4];
-      const unsigned ad[4] = {lds_addr(&red[0][mb][ln]), lds_addr(&red[1][mb][ln]), lds_addr(&red[2][mb][ln]),
-                              lds_addr(&red[3][mb][ln])};
-      lds_read_b128x4(t, ad);
-      sc[mb] = __builtin_bit_cast(f32x4, t[0]) + __builtin_bit_cast(f32x4, t[1]) + __builtin_bit_cast(f32x4, t[2]) +
-               __builtin_bit_cast(f32x4, t[3]);
-    }
-
-    // keys k0 + 16*mb + 4*G + jj for query n
-    float mx = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = k0 + 16 * mb + 4 * G + jj;
-        if (key >= k_end) sc[mb][jj] = kNegInf;
-        mx = fmaxf(mx, sc[mb][jj]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_i - m_use);
-    float p[2][4];
-    float rs = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        p[mb][jj] = fast_exp2(sc[mb][jj] - m_use);
-        rs += p[mb][jj];
-      }
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-    const bf16x8 pf = as_bf16x8(u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                                      pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])});
-
-    const char* vb = reinterpret_cast<const char*>(sbuf[stg][NT - 1]);
-    const int row1 = 4 * oG + (on >> 2), row2 = row1 + 16;
-    const unsigned v1 = lds_addr(vb + row1 * ROWB), v2 = lds_addr(vb + row2 * ROWB);
-    const int sw1 = swz(row1), sw2 = swz(row2);
-#pragma unroll
-    for (int b0 = 0; b0 < DBLK; b0 += 4) {
-      unsigned ad[8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
         const int dcol = wave * DQ + 16 * (b0 + u) + 4 * (on & 3);
-        const int chunk = dcol >> 3, half = (dcol & 7) << 1;
-        ad[2 * u] = v1 + ((chunk ^ sw1) << 4) + half;
-        ad[2 * u + 1] = v2 + ((chunk ^ sw2) << 4) + half;
+        ad[u] = va + (((dcol >> 3) ^ vsw) << 4) + ((dcol & 7) << 1);
       }
-      u32x2 t[8];
-      lds_read_tr_x8(t, ad);
+      u32x2 t[4];
+      lds_read_tr_x4(t, ad);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[b0 + u] = mfma16(cat2(t[2 * u], t[2 * u + 1]), pf, acc[b0 + u] * alpha);
+      for (int u = 0; u < 4; ++u) acc[b0 + u] = mfma16k16(t[u], pf, acc[b0 + u]);
     }
   }
 
-  float l = l_i + __shfl_xor(l_i, 16);
-  l += __shfl_xor(l, 32);
+  const float l = sum_over_groups(l_i);
   const float inv = 1.f / l;
   if (qvalid) {
     float* o = a.part_o + part * D + wave * DQ + 4 * G;
@@ -702,25 +909,58 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   }
 }
 
-// Log-sum-exp merge of the chunk partials of one (batch, head).
+// Log-sum-exp merge of the chunk partials of one (batch, head).  256
+// threads: thread t owns head-dim quad t % (D/4) and every (256/(D/4))-th
+// chunk starting at t / (D/4); the chunk groups are summed through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_lse, float* __restrict__ out,
                                                         int nchunks) {
+  constexpr int NQ = D / 4;        // head-dim quads
+  constexpr int NGRP = 256 / NQ;   // chunk groups
+  __shared__ f32x4 snum[NGRP][NQ];
+  __shared__ float sden[NGRP][NQ];
   const int bh = blockIdx.x;
+  const int qd = threadIdx.x % NQ, grp = threadIdx.x / NQ;
   const float* lse = part_lse + (size_t)bh * nchunks;
   float M = kNegInf;
   for (int c = 0; c < nchunks; ++c) M = fmaxf(M, lse[c]);
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      const float e = lse[c];
-      if (e == kNegInf) continue;
-      const float w = fast_exp2(e - M);
-      num += w * part_o[((size_t)bh * nchunks + c) * D + d];
-      den += w;
+  const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (size_t)bh * nchunks * D) + qd;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  int c = grp;
+  for (; c + 3 * NGRP < nchunks; c += 4 * NGRP) {
+    f32x4 o[4];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float e = lse[c + u * NGRP];
+      w[u] = e == kNegInf ? 0.f : fast_exp2(e - M);
+      o[u] = e == kNegInf ? f32x4{0.f, 0.f, 0.f, 0.f} : po[(size_t)(c + u * NGRP) * NQ];
     }
-    out[(size_t)bh * D + d] = num / den;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      num += w[u] * o[u];
+      den += w[u];
+    }
+  }
+  for (; c < nchunks; c += NGRP) {
+    const float e = lse[c];
+    if (e == kNegInf) continue;
+    const float w = fast_exp2(e - M);
+    num += w * po[(size_t)c * NQ];
+    den += w;
+  }
+  snum[grp][qd] = num;
+  sden[grp][qd] = den;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int g2 = 1; g2 < NGRP; ++g2) {
+      num += snum[g2][qd];
+      den += sden[g2][qd];
+    }
+    reinterpret_cast<f32x4*>(out + (size_t)bh * D)[qd] = num * (1.f / den);
   }
 }
 
@@ -736,42 +976,79 @@ void fill_rope_rev(RopeRev* r, int head_dim, double theta) {
     r->rev[f] = f < head_dim / 2 ? std::pow(theta, -2.0 * (double)f / (double)head_dim) / two_pi : 0.0;
 }
 
-size_t prefill_workspace(int B, int S, int Hkv, int D) {
-  const int BN = prefill_key_tile(D);
-  const size_t ntiles = (size_t)ceil_div(S, BN);
-  return (size_t)B * Hkv * ntiles * BN * D * 2;
+// Key tiles a 128-row query tile visits (same rule as the kernel).
+static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int& jlo, int& jhi) {
+  const int rows_total = S * g, r0 = qt * kPrefillRows;
+  const int pmin = r0 / g, pmax = std::min(r0 + kPrefillRows - 1, rows_total - 1) / g;
+  jlo = (W > 0 ? std::max(0, pmin - W + 1) : 0) / BN;
+  jhi = pmax / BN;
 }
 
+PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
+  PrefillPlan p;
+  p.BN = prefill_key_tile(D);
+  p.ntiles = ceil_div(S, p.BN);
+  p.g = Hq / Hkv;
+  p.nqt = ceil_div(S * p.g, kPrefillRows);
+  p.npair = (p.nqt + 1) / 2;
+  // largest key-work of a pair bounds the useful number of pieces
+  int umax = 1;
+  for (int i = 0; i < p.npair; ++i) {
+    int a0, a1, b0 = 0, b1 = -1;
+    prefill_tile_keys(p.nqt - 1 - i, S, p.g, W, p.BN, a0, a1);
+    if (i < p.nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, b0, b1);
+    umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
+  }
+  const long groups = (long)B * Hkv * p.npair;
+  p.kpieces = (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
+  p.kimg_bytes = (size_t)B * Hkv * p.ntiles * p.BN * D * 2;
+  p.counters_off = (p.kimg_bytes + 255) / 256 * 256;
+  p.ncounters = (size_t)B * Hkv * p.nqt;
+  p.part_off = (p.counters_off + p.ncounters * 4 + 255) / 256 * 256;
+  const int nw = 4 * prefill_dsplit(D);
+  p.slot_bytes = (size_t)32 * D * 16 + (size_t)nw * 64 * 2 * 4;  // accumulators + (m, l) per wave and lane
+  p.nslots = p.kpieces > 1 ? (size_t)groups * p.kpieces * 2 : 0;
+  p.total = p.part_off + p.nslots * p.slot_bytes;
+  return p;
+}
+
+size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W) { return plan_prefill(B, S, Hq, Hkv, D, W).total; }
+
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const ProfileEvents& ev) {
-  const int BN = prefill_key_tile(p.D);
-  const int ntiles = ceil_div(p.S, BN);
-  const int g = p.Hq / p.Hkv;
+  const PrefillPlan pl = plan_prefill(p.B, p.S, p.Hq, p.Hkv, p.D, p.W);
+  char* ws = static_cast<char*>(p.kimg);
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(p.q);
-  a.kimg = static_cast<const uint16_t*>(p.kimg);
+  a.kimg = reinterpret_cast<const uint16_t*>(ws);
   a.v = static_cast<const uint16_t*>(p.v);
   a.out = p.out;
+  a.counters = reinterpret_cast<int*>(ws + pl.counters_off);
+  a.part = reinterpret_cast<float*>(ws + pl.part_off);
   a.B = p.B;
   a.S = p.S;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
-  a.g = g;
+  a.g = pl.g;
   a.Lmax = p.Lmax;
   a.W = p.W;
-  a.ntiles = ntiles;
-  a.nqt = ceil_div(p.S * g, kPrefillRows);
+  a.ntiles = pl.ntiles;
+  a.nqt = pl.nqt;
+  a.npair = pl.npair;
+  a.kpieces = pl.kpieces;
   a.qscale = p.scale * kLog2e;
   fill_rope_rev(&a.rope, p.D, p.theta);
-  const dim3 grid_k(ntiles, p.Hkv, p.B);
-  const dim3 grid_a(a.nqt * p.B * p.Hkv);
+  const dim3 grid_k(pl.ntiles, p.Hkv, p.B);
+  const dim3 grid_a((unsigned)((long)p.B * p.Hkv * pl.npair * pl.kpieces));
   if (p.D == 512) {
     hipLaunchKernelGGL((k_rope_keys<512, 32>), grid_k, dim3(256), 0, stream, static_cast<const uint16_t*>(p.k),
-                       static_cast<uint16_t*>(p.kimg), p.S, p.Hkv, p.Lmax, ntiles, a.rope);
+                       reinterpret_cast<uint16_t*>(ws), p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters,
+                       (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     hipLaunchKernelGGL((k_prefill<512, 32, 2>), grid_a, dim3(512), 0, stream, a);
   } else {
     hipLaunchKernelGGL((k_rope_keys<256, 64>), grid_k, dim3(256), 0, stream, static_cast<const uint16_t*>(p.k),
-                       static_cast<uint16_t*>(p.kimg), p.S, p.Hkv, p.Lmax, ntiles, a.rope);
+                       reinterpret_cast<uint16_t*>(ws), p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters,
+                       (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     hipLaunchKernelGGL((k_prefill<256, 64, 1>), grid_a, dim3(256), 0, stream, a);
   }
@@ -821,14 +1098,14 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   if (ev.before) (void)hipEventRecord(ev.before, stream);
   if (p.D == 512) {
     if (p.alias)
-      hipLaunchKernelGGL((k_decode<512, true, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_decode<512, true, kDecodeStages>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((k_decode<512, false, 2>), grid, dim3(256), 0, stream, a);
   } else {
     if (p.alias)
-      hipLaunchKernelGGL((k_decode<256, true, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_decode<256, true, kDecodeStages>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_decode<256, false, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_decode<256, false, kDecodeStages>), grid, dim3(256), 0, stream, a);
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   if (p.D == 512)

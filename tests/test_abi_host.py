@@ -110,11 +110,45 @@ def test_kv_bytes_and_sharing(lib):
     assert total_k + total_v == 12 * 2048 * 256 * 2 + 3 * 2 * (2 * 2048 * 512 * 2) == 37748736
 
 
+def _prefill_ws_model(B, S, Hq, Hkv, D, W):
+    """Workspace layout of a prefill call: rotated key tiles, arrival counters,
+    partial-result slots of the query tiles split across work-groups."""
+    BN = 32 if D == 512 else 64
+    ntiles = -(-S // BN)
+    g = Hq // Hkv
+    nqt = -(-(S * g) // 128)
+    npair = (nqt + 1) // 2
+
+    def keys(qt):
+        r0 = qt * 128
+        pmin, pmax = r0 // g, min(r0 + 127, S * g - 1) // g
+        return (max(0, pmin - W + 1) if W > 0 else 0) // BN, pmax // BN
+
+    umax = 1
+    for i in range(npair):
+        a0, a1 = keys(nqt - 1 - i)
+        b0, b1 = keys(i) if i < nqt - 1 - i else (0, -1)
+        umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
+    groups = B * Hkv * npair
+    k = max(1, min(256 // groups, umax, 64))
+    kimg = B * Hkv * ntiles * BN * D * 2
+    cnt = -(-kimg // 256) * 256
+    part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256
+    nw = 8 if D == 512 else 4
+    slot = 32 * D * 16 + nw * 64 * 2 * 4
+    return part + (groups * k * 2 * slot if k > 1 else 0), k
+
+
 def test_workspace_sizes(lib):
     stack = wl.gemma4_stack()
-    assert L.prefill_workspace_bytes(stack, 4, 1, 2048) == 1 * 2 * 2048 * 512 * 2
-    assert L.prefill_workspace_bytes(stack, 0, 1, 2048) == 1 * 1 * 2048 * 256 * 2
-    assert L.prefill_workspace_bytes(stack, 0, 1, 100) == 1 * 1 * 128 * 256 * 2  # padded to the key tile
+    for layer in (0, 4):
+        d = stack[layer]
+        for S in (1, 100, 2048, 4096):
+            want, _ = _prefill_ws_model(1, S, d["num_q_heads"], d["num_kv_heads"], d["head_dim"], d["window"])
+            assert L.prefill_workspace_bytes(stack, layer, 1, S) == want
+    # the 4096-token full layer is cut into two pieces per pair of query tiles
+    assert _prefill_ws_model(1, 4096, 8, 2, 512, 0)[1] == 2
+    assert L.prefill_workspace_bytes(stack, 0, 1, 2048) >= 1 * 1 * 2048 * 256 * 2
     w = L.decode_workspace_bytes(stack, 4, 64, 8192)
     assert w > 0 and w % 4 == 0
     with pytest.raises(L.Gemma4Error):
