@@ -14,7 +14,9 @@ The line also carries:
                 same workload;
   decode        batched decode (64 sequences x 8192 cached tokens, full layer
                 head size 512 plus sliding K=V layer head size 256): KV bytes
-                per second of the split-K kernel against HBM peak.
+                per second of the split-K kernel against HBM peak;
+  stack         the 35-layer prefill stack (2048 tokens): every layer's call
+                in order, with the sliding and full layers also timed apart.
 """
 import argparse
 import json
@@ -192,6 +194,51 @@ def bench_decode(steps, warmup):
     }
 
 
+def bench_stack(steps):
+    """35-layer prefill stack (B=1, S=2048; 28 sliding hd256 W512 K=V + 7 full hd512, 15 owned caches):
+    one pass = every layer's prefill call, in order, on one stream."""
+    import torch
+    from hybrid_sliding_global_amd import Stack, inputs
+    from hybrid_sliding_global_amd import workloads as wl
+    w = wl.workloads()[4]
+    S = w.seq_len
+    st = Stack(w.layers)
+    qs, ks, vs, outs, wss = [], [], [], [], []
+    for i, d in enumerate(w.layers):
+        D = d["head_dim"]
+        qs.append(dev(inputs.normal_bf16([4, i, inputs.TENSOR_Q], (1, S, d["num_q_heads"], D))))
+        own = d["kv_source_layer"] < 0
+        ks.append(dev(inputs.normal_bf16([4, i, inputs.TENSOR_K], (1, d["num_kv_heads"], S, D))) if own else None)
+        vs.append(dev(inputs.normal_bf16([4, i, inputs.TENSOR_V], (1, d["num_kv_heads"], S, D)))
+                  if own and not d["kv_alias"] else None)
+        outs.append(torch.empty((1, S, d["num_q_heads"], D), dtype=torch.float32, device="cuda:0"))
+        wss.append(torch.empty(st.prefill_workspace_bytes(i, 1, S), dtype=torch.uint8, device="cuda:0"))
+    flops = sum(wl.prefill_flops(S, d["num_q_heads"], d["head_dim"], d["window"]) for d in w.layers)
+    sl_flops = sum(wl.prefill_flops(S, d["num_q_heads"], d["head_dim"], d["window"]) for d in w.layers
+                   if d["kind"] == wl.SLIDING)
+
+    def one_pass(which=None):
+        for i, d in enumerate(w.layers):
+            if which is None or d["kind"] == which:
+                st.prefill(i, qs[i], ks, vs, out=outs[i], workspace=wss[i])
+
+    res = {}
+    for tag, which, fl in (("stack", None, flops), ("sliding_layers", wl.SLIDING, sl_flops),
+                           ("full_layers", wl.FULL, flops - sl_flops)):
+        for _ in range(2):
+            one_pass(which)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            one_pass(which)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[tag] = {"ms_per_pass": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12, "algorithmic_flops": fl}
+    return {"workload": "stack35_prefill_s2048", **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,9 +246,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: the attention path has no multi-GPU code (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -224,6 +272,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_prefill<512,32,2>")},
     }
+    if not args.no_stack:
+        log("stack: 35-layer prefill S=2048")
+        line["stack"] = bench_stack(max(3, args.steps // 4))
+        log("stack: %.3f ms per pass (%.1f TFLOP/s)" % (line["stack"]["stack"]["ms_per_pass"],
+                                                        line["stack"]["stack"]["TFLOP/s"]))
     if not args.no_decode:
         log("decode: B=64 L=8192")
         line["decode"] = bench_decode(max(5, args.steps // 2), 2)

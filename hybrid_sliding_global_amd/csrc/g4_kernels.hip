@@ -526,57 +526,70 @@ k_prefill(PrefillArgs a) {
         return reinterpret_cast<f32x4*>(a.part) + (((size_t)bh * a.npair + pair) * a.kpieces + pc) * 2 * slot_f4 +
                (size_t)seg * slot_f4;
       };
-      f32x4* mine = slot_ptr(piece);
+      // Partials go through the device-coherent path (agent-scope relaxed
+      // atomics: stores write through the XCD's L2, loads do not trust it),
+      // so publishing them needs no L2-wide write-back or invalidation: wait
+      // for this work-group's stores, then bump the tile's counter.
+      float* mine = reinterpret_cast<float*>(slot_ptr(piece));
 #pragma unroll
       for (int db = 0; db < DBW; ++db)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          mine[((wave * DBW + db) * 4 + qd) * 64 + lane] =
-              f32x4{acc[db][4 * qd], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
-      float* ml = reinterpret_cast<float*>(mine + ACC_F4);
-      ml[wave * 64 + lane] = m_i;
-      ml[NW * 64 + wave * 64 + lane] = l_i;
-      __threadfence();
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __hip_atomic_store(mine + (((size_t)(wave * DBW + db) * 4 + qd) * 64 + lane) * 4 + e, acc[db][4 * qd + e],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float* ml = mine + (size_t)ACC_F4 * 4;
+      __hip_atomic_store(ml + wave * 64 + lane, m_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ml + NW * 64 + wave * 64 + lane, l_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // s_waitcnt: the stores above have landed
       __syncthreads();
-      int npieces = 0;
-      for (int pc = 0; pc < a.kpieces; ++pc) {
-        const int x0 = ubound(pc), x1 = ubound(pc + 1);
-        npieces += (x0 < x1 && x0 < ue && x1 > us) ? 1 : 0;
-      }
-      if (tid == 0) *s_last = atomicAdd(&a.counters[(size_t)bh * a.nqt + qt], 1) == npieces - 1;
-      __syncthreads();
-      const bool last = *s_last != 0;
-      __syncthreads();  // the buffer is refilled by the next segment
-      if (!last) return;
-      __threadfence();
-      // Deterministic merge: the result must not depend on which piece came
-      // last, so every piece (this one re-read from its own slot) is added in
-      // ascending piece order against the common maximum of all pieces.
       auto is_piece = [&](int pc) {
         const int x0 = ubound(pc), x1 = ubound(pc + 1);
         return x0 < x1 && x0 < ue && x1 > us;
       };
+      int npieces = 0;
+      for (int pc = 0; pc < a.kpieces; ++pc) npieces += is_piece(pc) ? 1 : 0;
+      // The arrival flag lives in the first word of a key buffer: no tile is
+      // in flight when it is written and read.
+      int* s_last = reinterpret_cast<int*>(sk0);
+      if (tid == 0)
+        *s_last = __hip_atomic_fetch_add(&a.counters[(size_t)bh * a.nqt + qt], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+      __syncthreads();
+      const bool last = *s_last != 0;
+      __syncthreads();  // the buffer is refilled by the next segment
+      if (!last) return;
+      // Deterministic merge: the result must not depend on which piece came
+      // last, so every piece (this one re-read from its own slot) is added in
+      // ascending piece order against the common maximum of all pieces.
       float M = kNegInf;
       for (int pc = 0; pc < a.kpieces; ++pc)
-        if (is_piece(pc)) M = fmaxf(M, reinterpret_cast<const float*>(slot_ptr(pc) + ACC_F4)[wave * 64 + lane]);
+        if (is_piece(pc))
+          M = fmaxf(M, __hip_atomic_load(reinterpret_cast<const float*>(slot_ptr(pc) + ACC_F4) + wave * 64 + lane,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 #pragma unroll
       for (int db = 0; db < DBW; ++db) acc[db] = f32x16{};
       l_i = 0.f;
       for (int pc = 0; pc < a.kpieces; ++pc) {
         if (!is_piece(pc)) continue;
-        const f32x4* src = slot_ptr(pc);
-        const float* sml = reinterpret_cast<const float*>(src + ACC_F4);
-        const float mp = sml[wave * 64 + lane], lp = sml[NW * 64 + wave * 64 + lane];
+        const float* src = reinterpret_cast<const float*>(slot_ptr(pc));
+        const float* sml = src + (size_t)ACC_F4 * 4;
+        const float mp = __hip_atomic_load(sml + wave * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float lp =
+            __hip_atomic_load(sml + NW * 64 + wave * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float f = mp == kNegInf ? 0.f : fast_exp2(mp - M);
         l_i += lp * f;
 #pragma unroll
         for (int db = 0; db < DBW; ++db)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 o = src[((wave * DBW + db) * 4 + qd) * 64 + lane];
+          for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[db][4 * qd + e] += o[e] * f;
-          }
+            for (int e = 0; e < 4; ++e)
+              acc[db][4 * qd + e] +=
+                  __hip_atomic_load(src + (((size_t)(wave * DBW + db) * 4 + qd) * 64 + lane) * 4 + e, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) *
+                  f;
       }
       m_i = M;
     }
