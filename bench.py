@@ -130,21 +130,21 @@ def cpu_baseline(pre, budget_s=15.0):
     d = w.layers[0]
     S, Hq, D = w.seq_len, d["num_q_heads"], d["head_dim"]
     rng = np.random.default_rng(0)
-    # grow the sample until it takes a few seconds, then extrapolate to the budget
+    # grow the sample of distinct rows until it takes a few seconds
     n = 8
     while True:
-        pos = np.sort(rng.integers(0, S, size=n))
-        heads = rng.integers(0, Hq, size=n)
-        rows = pos * Hq + heads
+        n = min(n, S * Hq)
+        rows = np.sort(rng.choice(S * Hq, size=n, replace=False))
+        pos = rows // Hq
         t0 = time.perf_counter()
         oracle.prefill(pre["q"], pre["k"], pre["v"], 0, d["rope_theta"], rows=rows)
         dt = time.perf_counter() - t0
-        if dt > budget_s / 4 or n >= 1 << 16:
+        if dt > budget_s / 4 or n == S * Hq:
             break
         n *= 2
     flops = float(sum(4 * D * (int(p) + 1) for p in pos))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "%d query rows (uniform positions and heads) of the 4096-token full-attention prefill, "
+            "sample": "%d distinct query rows (uniform over positions and heads) of the 4096-token full-attention prefill, "
                       "fp64, %.1f s" % (n, dt)}
 
 
@@ -222,20 +222,36 @@ def bench_stack(steps):
             if which is None or d["kind"] == which:
                 st.prefill(i, qs[i], ks, vs, out=outs[i], workspace=wss[i])
 
-    res = {}
-    for tag, which, fl in (("stack", None, flops), ("sliding_layers", wl.SLIDING, sl_flops),
-                           ("full_layers", wl.FULL, flops - sl_flops)):
+    def timed(fn):
         for _ in range(2):
-            one_pass(which)
+            fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            one_pass(which)
+            fn()
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        return e0.elapsed_time(e1) / steps
+
+    res = {}
+    for tag, which, fl in (("sliding_layers", wl.SLIDING, sl_flops), ("full_layers", wl.FULL, flops - sl_flops)):
+        ms = timed(lambda: one_pass(which))
         res[tag] = {"ms_per_pass": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12, "algorithmic_flops": fl}
+    eager_ms = timed(one_pass)
+    # the whole stack as one HIP graph (the library records no memset or allocation)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    ms = timed(graph.replay)
+    res["stack"] = {"ms_per_pass": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12, "algorithmic_flops": flops,
+                    "timing": "one HIP graph replay per pass", "eager_ms_per_pass": eager_ms}
     return {"workload": "stack35_prefill_s2048", **res}
 
 
@@ -247,6 +263,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (scale for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention path has no multi-GPU code (got --gpus %d)" % args.gpus,
@@ -256,6 +274,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
     log("prefill: full-attention layer B=1 S=4096 Hq=8 Hkv=2 D=512")
     pre = bench_prefill(args.steps, args.warmup)
     tflops = pre["flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
@@ -275,8 +302,9 @@ def main():
     if not args.no_stack:
         log("stack: 35-layer prefill S=2048")
         line["stack"] = bench_stack(max(3, args.steps // 4))
-        log("stack: %.3f ms per pass (%.1f TFLOP/s)" % (line["stack"]["stack"]["ms_per_pass"],
-                                                        line["stack"]["stack"]["TFLOP/s"]))
+        log("stack: %.3f ms per pass as one graph (%.1f TFLOP/s), %.3f ms eager" %
+            (line["stack"]["stack"]["ms_per_pass"], line["stack"]["stack"]["TFLOP/s"],
+             line["stack"]["stack"]["eager_ms_per_pass"]))
     if not args.no_decode:
         log("decode: B=64 L=8192")
         line["decode"] = bench_decode(max(5, args.steps // 2), 2)

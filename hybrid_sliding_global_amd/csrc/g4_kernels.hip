@@ -197,6 +197,22 @@ __device__ __forceinline__ f32x16 lds_read_f32x16(unsigned ad) {
   return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
 }
 
+// Four 16-byte stores of one lane's 16 accumulators to p, p + 1 KiB, p + 2 KiB
+// and p + 3 KiB through the device-coherent path (sc1: written through the
+// XCD's L2), so another XCD can read them after the writer's vmcnt drains.
+__device__ __forceinline__ void global_store_sc1_f32x16(float* p, const f32x16& v) {
+  const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+  const f32x4 c = {v[8], v[9], v[10], v[11]}, d = {v[12], v[13], v[14], v[15]};
+  asm volatile(
+      G4_MFMA_STORE_WAIT
+      "global_store_dwordx4 %0, %1, off sc1\n\t"
+      "global_store_dwordx4 %0, %2, off offset:1024 sc1\n\t"
+      "global_store_dwordx4 %0, %3, off offset:2048 sc1\n\t"
+      "global_store_dwordx4 %0, %4, off offset:3072 sc1" ::"v"(p),
+      "v"(a), "v"(b), "v"(c), "v"(d)
+      : "memory");
+}
+
 __device__ __forceinline__ i16x4 ds_read_tr(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
@@ -533,12 +549,7 @@ k_prefill(PrefillArgs a) {
       float* mine = reinterpret_cast<float*>(slot_ptr(piece));
 #pragma unroll
       for (int db = 0; db < DBW; ++db)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __hip_atomic_store(mine + (((size_t)(wave * DBW + db) * 4 + qd) * 64 + lane) * 4 + e, acc[db][4 * qd + e],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        global_store_sc1_f32x16(mine + ((size_t)(wave * DBW + db) * 4 * 64 + lane) * 4, acc[db]);
       float* ml = mine + (size_t)ACC_F4 * 4;
       __hip_atomic_store(ml + wave * 64 + lane, m_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ml + NW * 64 + wave * 64 + lane, l_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -150,6 +150,49 @@ def test_workload4_stack_sampled_rows_and_sharing():
         assert torch.equal(ref, outs[i]), "shared layer %d differs from a copied cache" % i
 
 
+def test_stack_graph_replays_match_eager():
+    """The 35-layer stack (S=640) captured in one HIP graph: every replay, with
+    eager calls and synchronisations in between, equals the eager outputs bit
+    for bit (the prefill kernels are deterministic)."""
+    import torch
+    S = 640
+    layers, qs, kc, vc = _stack_inputs(S)
+    st = Stack(layers)
+    kd = [None if k is None else to_dev(k) for k in kc]
+    vd = [None if v is None else to_dev(v) for v in vc]
+    qd = [to_dev(q) for q in qs]
+    outs = [torch.empty((1, S, d["num_q_heads"], d["head_dim"]), dtype=torch.float32, device="cuda:0")
+            for d in layers]
+    wss = [torch.empty(st.prefill_workspace_bytes(i, 1, S), dtype=torch.uint8, device="cuda:0")
+           for i in range(len(layers))]
+
+    def one_pass():
+        for i in range(len(layers)):
+            st.prefill(i, qd[i], kd, vd, out=outs[i], workspace=wss[i])
+
+    one_pass()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(len(layers)):
+            assert torch.equal(outs[i], eager[i]), "replay %d, layer %d differs from eager" % (rep, i)
+        one_pass()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_alias_equals_explicit_duplicate_values():
     import torch
     S, D = 300, 256
