@@ -28,10 +28,12 @@ inline int prefill_dsplit(int head_dim) { return head_dim == 512 ? 2 : 1; }
 constexpr int kPrefillSlots = 256;
 
 // How a prefill call is cut into work-groups and how its workspace is laid
-// out: [rotated key tiles][arrival counters][partial-result slots].
+// out: [key operand image][value operand image][arrival counters]
+// [partial-result slots]; each image is [B, Hkv, ntiles, BN * D] bf16.
 struct PrefillPlan {
   int BN = 0, ntiles = 0, g = 0, nqt = 0, npair = 0, kpieces = 0;
-  size_t kimg_bytes = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0, total = 0;
+  size_t kimg_bytes = 0, vimg_off = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0,
+         total = 0;
 };
 PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W);
 
@@ -40,7 +42,7 @@ struct PrefillLaunch {
   const void* k;      // bf16 raw keys [B, Hkv, Lmax, D]
   const void* v;      // bf16 values (== k for an aliased layer)
   float* out;         // fp32 [B, S, Hq, D]
-  void* kimg;         // workspace: rotated key tiles
+  void* kimg;         // workspace (operand images, counters, partial slots)
   int B, S, Hq, Hkv, D, Lmax, W;
   float scale;        // softmax scale (already resolved, > 0)
   double theta;

@@ -1,9 +1,10 @@
 // HIP kernels for gfx950 (CDNA4): Gemma-4-style hybrid sliding/global attention.
 //
 // Prefill = two launches on the caller's stream:
-//   1. k_rope_keys  : rotates the raw cached keys once (RoPE, the layer's own
-//                     theta) into a workspace image laid out exactly as the
-//                     attention kernel's LDS tiles (row-swizzled 16 B chunks);
+//   1. k_prefill_prep : rotates the raw cached keys once (RoPE, the layer's
+//                     own theta) and writes key and value operand images in
+//                     exactly the order the attention kernel's MFMA operands
+//                     are read from LDS (values transposed, not rotated);
 //   2. k_prefill    : flash-style causal / sliding-window attention on bf16
 //                     MFMA.  Each work-group owns 128 (position, head) query
 //                     rows of one (batch, kv-head) pair -- the GQA group shares
@@ -11,9 +12,8 @@
 //                     Scores are computed transposed, S^T = K' Q'^T, and the
 //                     output as O^T += V^T P^T, so every per-query softmax
 //                     quantity lives in one lane (plus its partner 32 lanes
-//                     away).  V is read straight from the cache through the
-//                     LDS transpose read (ds_read_b64_tr_b16); for an aliased
-//                     layer that buffer is the raw key cache.
+//                     away).  For an aliased layer the value image is built
+//                     from the raw key cache.
 // Decode = split-K over chunks of the visible key range:
 //   1. k_decode     : one work-group per (batch, kv-head, chunk); the four
 //                     waves split the head dimension, rotate keys on load,
@@ -234,32 +234,88 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // --------------------------------------------------------- prefill: keys --
 
-// Rotate raw keys rows [0, S) of one (batch, kv-head) slice into the tile
-// image: tile t holds rows t*BN .. t*BN+BN-1, each row's 16-byte chunks at
-// swizzled positions; rows >= S are zero.  Also clears the attention
+// Direct-to-LDS copy of one 1 KiB block: lane l moves 16 bytes from
+// gbase + voff (voff = 16 * l + block offset) to LDS lds + 16 * l.  Written
+// as asm on purpose: the compiler then does not see an LDS store, so it
+// schedules the plain LDS reads of the other buffer freely instead of
+// draining every outstanding copy (vmcnt(0)) in front of them.  The caller
+// waits for its own copies (wait_vm) before the barrier that publishes them.
+// M0 is clobbered here; no other code in these kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Operand images of one key tile, written once per prefill call so that the
+// attention kernel copies each tile into LDS linearly and reads every MFMA
+// operand as one conflict-free 1 KiB row of 16-byte lane slots:
+//
+//   key image, block (mb, ks) of 64 lane slots (block index mb * D/16 + ks):
+//     lane l holds RoPE(k)[32 mb + l % 32][16 ks + 8 (l / 32) + e], e < 8
+//     (the A operand of S^T = K' Q'^T for key block mb, head-dim step ks);
+//   value image, block (kv, db) (block index kv * D/32 + db):
+//     lane l holds v[16 kv + 4 (l / 32) + (e & 3) + 8 (e >> 2)][32 db + l % 32]
+//     (the A operand of O^T += V^T P^T for the 16-key step kv; this key order
+//     matches where the score layout leaves each probability).
+//
+// Values are not rotated (for an aliased layer `v` is the raw key buffer).
+// Rows at or beyond S are written as zeros.  Also clears the attention
 // kernel's arrival counters (this launch precedes it on the same stream).
 template <int D, int BN>
-__global__ __launch_bounds__(256) void k_rope_keys(const uint16_t* __restrict__ k, uint16_t* __restrict__ img, int S,
-                                                   int Hkv, int Lmax, int ntiles, RopeRev rope, int* counters,
-                                                   int ncounters) {
+__global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                      uint16_t* __restrict__ kimg, uint16_t* __restrict__ vimg, int S,
+                                                      int Hkv, int Lmax, int ntiles, RopeRev rope, int* counters,
+                                                      int ncounters) {
+  constexpr int KSTEPS = D / 16, DB = D / 32, KV = BN / 16;
+  constexpr int PITCH = D + 8;  // staged value row, bf16 elements (16-byte skew per row)
+  __shared__ __attribute__((aligned(16))) uint16_t sv[BN * PITCH];
   const int t = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int flat = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
   for (int i = flat * 256 + threadIdx.x; i < ncounters; i += gridDim.x * gridDim.y * gridDim.z * 256) counters[i] = 0;
-  const uint16_t* src = k + ((size_t)b * Hkv + kvh) * (size_t)Lmax * D;
-  uint16_t* dst = img + (((size_t)b * Hkv + kvh) * ntiles + t) * (size_t)(BN * D);
-  constexpr int CH = D / 16;  // chunk c pairs with chunk c + CH
+  const size_t slice = ((size_t)b * Hkv + kvh) * (size_t)Lmax * D;
+  const size_t tile = (((size_t)b * Hkv + kvh) * ntiles + t) * (size_t)(BN * D);
+  const uint16_t* ksrc = k + slice;
+  const uint16_t* vsrc = v + slice;
+  uint16_t* kdst = kimg + tile;
+  uint16_t* vdst = vimg + tile;
+
+  // keys: chunk c (8 elements at 8c) of the first half pairs with chunk c of the second half
+  constexpr int CH = D / 16;
   for (int it = threadIdx.x; it < BN * CH; it += 256) {
     const int row = it / CH, c = it % CH, p = t * BN + row;
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (p < S) {
-      const uint16_t* r = src + (size_t)p * D;
+      const uint16_t* r = ksrc + (size_t)p * D;
       x = *reinterpret_cast<const u32x4*>(r + 8 * c);
       y = *reinterpret_cast<const u32x4*>(r + D / 2 + 8 * c);
       rope8(x, y, rope.rev, 8 * c, (double)p, 1.0f);
     }
-    const int sw = swz(row);
-    *reinterpret_cast<u32x4*>(dst + row * D + 8 * (c ^ sw)) = x;
-    *reinterpret_cast<u32x4*>(dst + row * D + 8 * ((c + CH) ^ sw)) = y;
+    const int lane = (row & 31) + 32 * (c & 1), mb = row >> 5;
+    *reinterpret_cast<u32x4*>(kdst + ((mb * KSTEPS + (c >> 1)) * 64 + lane) * 8) = x;
+    *reinterpret_cast<u32x4*>(kdst + ((mb * KSTEPS + KSTEPS / 2 + (c >> 1)) * 64 + lane) * 8) = y;
+  }
+
+  // values: stage the tile's rows, then gather the transposed lane slots
+  for (int it = threadIdx.x; it < BN * (D / 8); it += 256) {
+    const int row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
+    u32x4 x = {0, 0, 0, 0};
+    if (p < S) x = *reinterpret_cast<const u32x4*>(vsrc + (size_t)p * D + 8 * c);
+    *reinterpret_cast<u32x4*>(sv + row * PITCH + 8 * c) = x;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < KV * DB * 64; it += 256) {
+    const int lane = it & 63, blk = it >> 6, kv = blk / DB, db = blk % DB;
+    const int d = 32 * db + (lane & 31), k0 = 16 * kv + 4 * (lane >> 5);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ka = k0 + ((2 * e) & 3) + 8 * ((2 * e) >> 2), kb = k0 + ((2 * e + 1) & 3) + 8 * ((2 * e + 1) >> 2);
+      o[e] = (unsigned)sv[ka * PITCH + d] | ((unsigned)sv[kb * PITCH + d] << 16);
+    }
+    *reinterpret_cast<u32x4*>(vdst + (blk * 64 + lane) * 8) = o;
   }
 }
 
@@ -267,8 +323,8 @@ __global__ __launch_bounds__(256) void k_rope_keys(const uint16_t* __restrict__ 
 
 struct PrefillArgs {
   const uint16_t* q;
-  const uint16_t* kimg;
-  const uint16_t* v;
+  const uint16_t* kimg;  // key operand image (see k_prefill_prep)
+  const uint16_t* vimg;  // value operand image
   float* out;
   int* counters;  // [B * Hkv * nqt] arrival counts (zeroed by the key pass)
   float* part;    // partial-result slots
@@ -304,24 +360,21 @@ k_prefill(PrefillArgs a) {
   constexpr int KSTEPS = D / 16;              // 32x32x16 steps over the head dim
   constexpr int KSW = KSTEPS / DS;            // steps owned by one wave
   constexpr int MB = BN / 32;                 // 32-key blocks per tile
+  constexpr int KV = BN / 16;                 // 16-key steps per tile
   constexpr int DB = D / 32;                  // 32-wide output blocks
   constexpr int DBW = DB / DS;                // output blocks owned by one wave
-  constexpr int LPT = BN * D * 2 / (NT * 16); // 16-byte loads per thread per tile and tensor
-  constexpr int ROWB = D * 2;
+  constexpr int TILE_BLKS = BN * D * 2 / 1024;  // 1 KiB blocks per operand tile
+  constexpr int LPT = TILE_BLKS / NW;         // blocks each wave copies per tile and operand
   constexpr int ACC_F4 = NW * DBW * 4 * 64;   // f32x4 per partial slot (accumulators)
-  static_assert(LPT * NT * 16 == BN * D * 2, "tile must split evenly over the threads");
+  static_assert(LPT * NW == TILE_BLKS, "tile must split evenly over the waves");
 
-  // Double-buffered key / value tiles.  The two buffers are distinct objects
-  // and the tile loop is unrolled by two, so the compiler can tell that the
-  // direct-to-LDS prefetch of the next tile never aliases the tile being read.
-  __shared__ __attribute__((aligned(16))) uint16_t sk0[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sk1[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sv0[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sv1[BN * D];
-  __shared__ f32x16 sx[DS > 1 ? NW : 1][MB][64];  // partial S^T exchange
-  // The arrival flag of a split tile lives in the first word of a key
-  // buffer: no tile is in flight when it is written and read.
-  int* s_last = reinterpret_cast<int*>(sk0);
+  // Double-buffered key / value operand tiles (layouts of k_prefill_prep).
+  __shared__ __attribute__((aligned(1024))) uint16_t sk0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sk1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv1[BN * D];
+  // Partial S^T exchange between the DS waves of a row group: [wave][mb][quad][lane].
+  __shared__ f32x4 sx[DS > 1 ? NW : 1][MB][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lives in SGPRs
@@ -352,30 +405,26 @@ k_prefill(PrefillArgs a) {
   auto ubound = [&](int j) { return (int)(((long long)j * U) / a.kpieces); };
   const int u0 = ubound(piece), u1 = ubound(piece + 1);
 
-  const uint16_t* kimg = a.kimg + (size_t)(b * a.Hkv + kvh) * a.ntiles * (size_t)(BN * D);
-  const uint16_t* vsl = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
+  const size_t slice_off = (size_t)(b * a.Hkv + kvh) * a.ntiles * (size_t)(BN * D);
+  const uint16_t* kimg = a.kimg + slice_off;
+  const uint16_t* vimg = a.vimg + slice_off;
+  const unsigned voff = (unsigned)(wave * 1024 + lane * 16);  // this lane's slot in the wave's first block
 
+  // Copy key tile j and value tile j into (dk, dv): this wave's blocks are i * NW + wave.
   auto issue = [&](int j, uint16_t* dk, uint16_t* dv) {
-    int ln = lane;  // opaque: keep the per-lane address math inside the loop
-    asm volatile("" : "+v"(ln));
-    const char* ksrc = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
+    const char* kt = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
+    const char* vt = reinterpret_cast<const char*>(vimg + (size_t)j * (BN * D));
+    const unsigned lk = lds_addr(dk) + wave * 1024, lv = lds_addr(dv) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int blk = i * NW + wave;
-      g2l16(ksrc + blk * 1024 + ln * 16, reinterpret_cast<char*>(dk) + blk * 1024);
-    }
+    for (int i = 0; i < LPT; ++i) dma_block(kt + i * NW * 1024, voff, lk + i * NW * 1024);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int blk = i * NW + wave;
-      const int byte = blk * 1024 + ln * 16;
-      const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
-      const int src_row = min(j * BN + row, a.S - 1);  // rows past the sequence: any valid row, weight 0
-      g2l16(vsl + (size_t)src_row * D + ((slot ^ swz(row)) << 3), reinterpret_cast<char*>(dv) + blk * 1024);
-    }
+    for (int i = 0; i < LPT; ++i) dma_block(vt + i * NW * 1024, voff, lv + i * NW * 1024);
   };
 
   // One segment: query tile qt against key tiles [jb, je]; seg = 0 (long) or 1 (short).
   auto process = [&](int qt, int seg, int jb, int je, int jlo_t, int jhi_t, int us, int ue) {
+    issue(jb, sk0, sv0);  // the first tile streams in while the queries are rotated
+
     const int r0 = qt * 128;
     const int r = r0 + rg * 32 + n;
     const bool valid = r < rows_total;
@@ -413,45 +462,35 @@ k_prefill(PrefillArgs a) {
       lds_barrier();  // everybody's share has, and tile j-1 is no longer being read
       if (j < je) issue(j + 1, nk, nv);
 
-      // Per-lane LDS offsets are recomputed every tile from an opaque copy of
-      // the lane index instead of being hoisted out of the loop, which would
-      // pin a few dozen registers for the whole kernel.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int on = ln & 31, oh = ln >> 5, oG = ln >> 4, oi16 = ln & 15;
-
       // S^T = K' Q'^T for this tile: s[mb] holds keys 32*mb + 8*i + 4*h + jj (reg 4*i + jj) of query n.
       f32x16 s[MB];
-      const char* kb = reinterpret_cast<const char*>(ck);
+      const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + lane;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         s[mb] = f32x16{};
-        const int row = 32 * mb + on;
-        const int sw = swz(row);
-        const unsigned kra = lds_addr(kb + row * ROWB);
 #pragma unroll
-        for (int i0 = 0; i0 < KSW; i0 += 4) {
-          unsigned ad[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u;
-            const int ks = i < KSW / 2 ? dp * (KSW / 2) + i : KSTEPS / 2 + dp * (KSW / 2) + (i - KSW / 2);
-            ad[u] = kra + (((2 * ks + oh) ^ sw) << 4);
-          }
-          u32x4 kf[4];
-          lds_read_b128x4(kf, ad);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) s[mb] = mfma32(as_bf16x8(kf[u]), qf[i0 + u], s[mb]);
+        for (int i = 0; i < KSW; ++i) {
+          const int ks = i < KSW / 2 ? dp * (KSW / 2) + i : KSTEPS / 2 + dp * (KSW / 2) + (i - KSW / 2);
+          s[mb] = mfma32(as_bf16x8(kb[(mb * KSTEPS + ks) * 64]), qf[i], s[mb]);
         }
       }
       if constexpr (DS > 1) {
         // exchange the two halves of the head-dim sum within the wave pair;
         // float addition is commutative, so both waves get identical scores
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) lds_write_f32x16(lds_addr(&sx[wave][mb][ln]), s[mb]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            sx[wave][mb][qd][lane] = f32x4{s[mb][4 * qd], s[mb][4 * qd + 1], s[mb][4 * qd + 2], s[mb][4 * qd + 3]};
         lds_barrier();
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) s[mb] += lds_read_f32x16(lds_addr(&sx[wave ^ 1][mb][ln]));
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 o = sx[wave ^ 1][mb][qd][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[mb][4 * qd + e] += o[e];
+          }
       }
 
       const int kbase = j * BN;
@@ -499,35 +538,18 @@ k_prefill(PrefillArgs a) {
         }
       l_i += rs;
 
-      // O^T += V^T P^T.  P^T slot t of key-step ks is key 16*ks + 4*hh + t (t < 4)
-      // or 16*ks + 8 + 4*hh + (t - 4); the transpose reads fetch V in that order.
-      const char* vb = reinterpret_cast<const char*>(cv);
-      const int ohh = oG >> 1, odsub = 16 * (oG & 1);
+      // O^T += V^T P^T.  P^T slot t of key-step kv is key 16*kv + 4*h + t (t < 4)
+      // or 16*kv + 8 + 4*h + (t - 4): the value image stores V in that order.
+      const u32x4* vb = reinterpret_cast<const u32x4*>(cv) + lane;
 #pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
-        const int row1 = 16 * ks + 4 * ohh + (oi16 >> 2), row2 = row1 + 8;
-        const unsigned v1 = lds_addr(vb + row1 * ROWB), v2 = lds_addr(vb + row2 * ROWB);
-        const int sw1 = swz(row1), sw2 = swz(row2);
+      for (int kv = 0; kv < KV; ++kv) {
+        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]});
 #pragma unroll
-        for (int i0 = 0; i0 < DBW; i0 += 4) {
-          unsigned ad[8];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int dcol = 32 * (dp * DBW + i0 + u) + odsub + 4 * (oi16 & 3);
-            const int chunk = dcol >> 3, half = (dcol & 7) << 1;
-            ad[2 * u] = v1 + ((chunk ^ sw1) << 4) + half;
-            ad[2 * u + 1] = v2 + ((chunk ^ sw2) << 4) + half;
-          }
-          u32x2 t[8];
-          lds_read_tr_x8(t, ad);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[i0 + u] = mfma32(cat2(t[2 * u], t[2 * u + 1]), pf, acc[i0 + u]);
-        }
+        for (int db = 0; db < DBW; ++db)
+          acc[db] = mfma32(as_bf16x8(vb[(kv * DB + dp * DBW + db) * 64]), pf, acc[db]);
       }
     };
 
-    issue(jb, sk0, sv0);
     for (int j = jb;;) {
       step(j, sk0, sv0, sk1, sv1);
       if (++j > je) break;
@@ -1026,7 +1048,8 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   const long groups = (long)B * Hkv * p.npair;
   p.kpieces = (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
   p.kimg_bytes = (size_t)B * Hkv * p.ntiles * p.BN * D * 2;
-  p.counters_off = (p.kimg_bytes + 255) / 256 * 256;
+  p.vimg_off = (p.kimg_bytes + 255) / 256 * 256;
+  p.counters_off = p.vimg_off + (p.kimg_bytes + 255) / 256 * 256;
   p.ncounters = (size_t)B * Hkv * p.nqt;
   p.part_off = (p.counters_off + p.ncounters * 4 + 255) / 256 * 256;
   const int nw = 4 * prefill_dsplit(D);
@@ -1044,7 +1067,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(p.q);
   a.kimg = reinterpret_cast<const uint16_t*>(ws);
-  a.v = static_cast<const uint16_t*>(p.v);
+  a.vimg = reinterpret_cast<const uint16_t*>(ws + pl.vimg_off);
   a.out = p.out;
   a.counters = reinterpret_cast<int*>(ws + pl.counters_off);
   a.part = reinterpret_cast<float*>(ws + pl.part_off);
@@ -1063,16 +1086,18 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   fill_rope_rev(&a.rope, p.D, p.theta);
   const dim3 grid_k(pl.ntiles, p.Hkv, p.B);
   const dim3 grid_a((unsigned)((long)p.B * p.Hkv * pl.npair * pl.kpieces));
+  const uint16_t* kraw = static_cast<const uint16_t*>(p.k);
+  const uint16_t* vraw = static_cast<const uint16_t*>(p.v);
+  uint16_t* kimg = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* vimg = reinterpret_cast<uint16_t*>(ws + pl.vimg_off);
   if (p.D == 512) {
-    hipLaunchKernelGGL((k_rope_keys<512, 32>), grid_k, dim3(256), 0, stream, static_cast<const uint16_t*>(p.k),
-                       reinterpret_cast<uint16_t*>(ws), p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters,
-                       (int)pl.ncounters);
+    hipLaunchKernelGGL((k_prefill_prep<512, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
+                       p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     hipLaunchKernelGGL((k_prefill<512, 32, 2>), grid_a, dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_rope_keys<256, 64>), grid_k, dim3(256), 0, stream, static_cast<const uint16_t*>(p.k),
-                       reinterpret_cast<uint16_t*>(ws), p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters,
-                       (int)pl.ncounters);
+    hipLaunchKernelGGL((k_prefill_prep<256, 64>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
+                       p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     hipLaunchKernelGGL((k_prefill<256, 64, 1>), grid_a, dim3(256), 0, stream, a);
   }

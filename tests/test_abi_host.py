@@ -111,8 +111,9 @@ def test_kv_bytes_and_sharing(lib):
 
 
 def _prefill_ws_model(B, S, Hq, Hkv, D, W):
-    """Workspace layout of a prefill call: rotated key tiles, arrival counters,
-    partial-result slots of the query tiles split across work-groups."""
+    """Workspace layout of a prefill call: key and value operand images,
+    arrival counters, partial-result slots of the query tiles split across
+    work-groups."""
     BN = 32 if D == 512 else 64
     ntiles = -(-S // BN)
     g = Hq // Hkv
@@ -131,8 +132,8 @@ def _prefill_ws_model(B, S, Hq, Hkv, D, W):
         umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
     groups = B * Hkv * npair
     k = max(1, min(256 // groups, umax, 64))
-    kimg = B * Hkv * ntiles * BN * D * 2
-    cnt = -(-kimg // 256) * 256
+    img = -(-(B * Hkv * ntiles * BN * D * 2) // 256) * 256
+    cnt = 2 * img
     part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256
     nw = 8 if D == 512 else 4
     slot = 32 * D * 16 + nw * 64 * 2 * 4
