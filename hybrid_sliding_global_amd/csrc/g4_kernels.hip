@@ -50,6 +50,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // log2 units
+#ifndef G4_PIPE_DEPTH
+#define G4_PIPE_DEPTH 4
+#endif
 constexpr int kDecodeStages = 4;      // 16-row key/value stages in the decode LDS ring (2 when K and V
                                       // are both staged at head size 512, so two work-groups share a CU)
 
@@ -197,22 +200,6 @@ __device__ __forceinline__ f32x16 lds_read_f32x16(unsigned ad) {
   return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
 }
 
-// Four 16-byte stores of one lane's 16 accumulators to p, p + 1 KiB, p + 2 KiB
-// and p + 3 KiB through the device-coherent path (sc1: written through the
-// XCD's L2), so another XCD can read them after the writer's vmcnt drains.
-__device__ __forceinline__ void global_store_sc1_f32x16(float* p, const f32x16& v) {
-  const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
-  const f32x4 c = {v[8], v[9], v[10], v[11]}, d = {v[12], v[13], v[14], v[15]};
-  asm volatile(
-      G4_MFMA_STORE_WAIT
-      "global_store_dwordx4 %0, %1, off sc1\n\t"
-      "global_store_dwordx4 %0, %2, off offset:1024 sc1\n\t"
-      "global_store_dwordx4 %0, %3, off offset:2048 sc1\n\t"
-      "global_store_dwordx4 %0, %4, off offset:3072 sc1" ::"v"(p),
-      "v"(a), "v"(b), "v"(c), "v"(d)
-      : "memory");
-}
-
 __device__ __forceinline__ i16x4 ds_read_tr(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
@@ -231,6 +218,21 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scheduling hint for a block of N MFMAs, each fed by one LDS read: keep P
+// reads in flight ahead of the MFMAs (P reads, then N - P (MFMA, read)
+// pairs, then the last P MFMAs).  Without it the scheduler keeps only two
+// reads ahead and every MFMA waits out the LDS latency.
+template <int N, int P>
+__device__ __forceinline__ void lds_mfma_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, P, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
+}
 
 // --------------------------------------------------------- prefill: keys --
 
@@ -367,6 +369,7 @@ k_prefill(PrefillArgs a) {
   constexpr int LPT = TILE_BLKS / NW;         // blocks each wave copies per tile and operand
   constexpr int ACC_F4 = NW * DBW * 4 * 64;   // f32x4 per partial slot (accumulators)
   static_assert(LPT * NW == TILE_BLKS, "tile must split evenly over the waves");
+  constexpr int kPipeDepth = G4_PIPE_DEPTH;  // LDS operand reads kept in flight ahead of the MFMAs
 
   // Double-buffered key / value operand tiles (layouts of k_prefill_prep).
   __shared__ __attribute__((aligned(1024))) uint16_t sk0[BN * D];
@@ -410,15 +413,22 @@ k_prefill(PrefillArgs a) {
   const uint16_t* vimg = a.vimg + slice_off;
   const unsigned voff = (unsigned)(wave * 1024 + lane * 16);  // this lane's slot in the wave's first block
 
-  // Copy key tile j and value tile j into (dk, dv): this wave's blocks are i * NW + wave.
-  auto issue = [&](int j, uint16_t* dk, uint16_t* dv) {
+  // Copy key tile j into dk / value tile j into dv: this wave's blocks are i * NW + wave.
+  auto issue_k = [&](int j, uint16_t* dk) {
     const char* kt = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
-    const char* vt = reinterpret_cast<const char*>(vimg + (size_t)j * (BN * D));
-    const unsigned lk = lds_addr(dk) + wave * 1024, lv = lds_addr(dv) + wave * 1024;
+    const unsigned lk = lds_addr(dk) + wave * 1024;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) dma_block(kt + i * NW * 1024, voff, lk + i * NW * 1024);
+  };
+  auto issue_v = [&](int j, uint16_t* dv) {
+    const char* vt = reinterpret_cast<const char*>(vimg + (size_t)j * (BN * D));
+    const unsigned lv = lds_addr(dv) + wave * 1024;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) dma_block(vt + i * NW * 1024, voff, lv + i * NW * 1024);
+  };
+  auto issue = [&](int j, uint16_t* dk, uint16_t* dv) {
+    issue_k(j, dk);
+    issue_v(j, dv);
   };
 
   // One segment: query tile qt against key tiles [jb, je]; seg = 0 (long) or 1 (short).
@@ -457,13 +467,9 @@ k_prefill(PrefillArgs a) {
     for (int i = 0; i < DBW; ++i) acc[i] = f32x16{};
     float m_i = kNegInf, l_i = 0.f;
 
-    auto step = [&](int j, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
-      wait_vm<0>();  // this wave's share of tile j has landed
-      lds_barrier();  // everybody's share has, and tile j-1 is no longer being read
-      if (j < je) issue(j + 1, nk, nv);
-
-      // S^T = K' Q'^T for this tile: s[mb] holds keys 32*mb + 8*i + 4*h + jj (reg 4*i + jj) of query n.
-      f32x16 s[MB];
+    // S^T = K' Q'^T for one tile (this wave's head-dim steps): s[mb] holds
+    // keys 32*mb + 8*i + 4*h + jj (reg 4*i + jj) of query n.
+    auto scores = [&](const uint16_t* ck, f32x16 (&s)[MB]) {
       const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + lane;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -474,25 +480,31 @@ k_prefill(PrefillArgs a) {
           s[mb] = mfma32(as_bf16x8(kb[(mb * KSTEPS + ks) * 64]), qf[i], s[mb]);
         }
       }
-      if constexpr (DS > 1) {
-        // exchange the two halves of the head-dim sum within the wave pair;
-        // float addition is commutative, so both waves get identical scores
+      lds_mfma_pipeline<MB * KSW, kPipeDepth>();
+    };
+    // The two halves of a head-dim sum meet in LDS: each wave of a pair
+    // publishes its partial scores, and after a barrier adds the partner's
+    // (float addition is commutative, so both waves get identical scores).
+    auto publish = [&](const f32x16 (&s)[MB]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            sx[wave][mb][qd][lane] = f32x4{s[mb][4 * qd], s[mb][4 * qd + 1], s[mb][4 * qd + 2], s[mb][4 * qd + 3]};
-        lds_barrier();
+        for (int qd = 0; qd < 4; ++qd)
+          sx[wave][mb][qd][lane] = f32x4{s[mb][4 * qd], s[mb][4 * qd + 1], s[mb][4 * qd + 2], s[mb][4 * qd + 3]};
+    };
+    auto add_partner = [&](f32x16 (&s)[MB]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 o = sx[wave ^ 1][mb][qd][lane];
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 o = sx[wave ^ 1][mb][qd][lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[mb][4 * qd + e] += o[e];
-          }
-      }
+          for (int e = 0; e < 4; ++e) s[mb][4 * qd + e] += o[e];
+        }
+    };
 
+    // Mask, online softmax and O^T += V^T P^T for key tile j.
+    auto softmax_pv = [&](int j, f32x16 (&s)[MB], const uint16_t* cv) {
       const int kbase = j * BN;
       const bool need_mask = (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
       if (need_mask) {
@@ -548,13 +560,65 @@ k_prefill(PrefillArgs a) {
         for (int db = 0; db < DBW; ++db)
           acc[db] = mfma32(as_bf16x8(vb[(kv * DB + dp * DBW + db) * 64]), pf, acc[db]);
       }
+      lds_mfma_pipeline<KV * DBW, kPipeDepth>();
     };
 
-    for (int j = jb;;) {
-      step(j, sk0, sv0, sk1, sv1);
-      if (++j > je) break;
-      step(j, sk1, sv1, sk0, sv0);
-      if (++j > je) break;
+    if constexpr (DS == 1) {
+      auto step = [&](int j, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
+        wait_vm<0>();  // this wave's share of tile j has landed
+        lds_barrier();  // everybody's share has, and tile j-1 is no longer being read
+        if (j < je) issue(j + 1, nk, nv);
+        f32x16 s[MB];
+        scores(ck, s);
+        softmax_pv(j, s, cv);
+      };
+      for (int j = jb;;) {
+        step(j, sk0, sv0, sk1, sv1);
+        if (++j > je) break;
+        step(j, sk1, sv1, sk0, sv0);
+        if (++j > je) break;
+      }
+    } else {
+      // Two wave groups (waves 0-3 and 4-7, one of each per SIMD) run the
+      // same tile sequence half a step apart: in every phase one group
+      // computes scores for tile i while the other finishes tile i-1
+      // (partner scores, softmax, PV), so each SIMD always has MFMA work
+      // from one wave while the other waits on LDS or runs the softmax.
+      // Phase t: group g works on u = t - g; even u = scores of tile jb + u/2,
+      // odd u = softmax and PV of tile jb + (u-1)/2.  Key tile j lives in
+      // buffer (j - jb) & 1 during phases 2(j-jb) .. 2(j-jb)+1 and value tile
+      // j during phases 2(j-jb)+1 .. 2(j-jb)+2; the next key tile is copied
+      // at the start of even phases and the next value tile at the start of
+      // odd ones, each into the buffer its predecessor has just left.
+      const int grp = wave >> 2;
+      const int nt = je - jb + 1;
+      auto phase_begin = [&](int t) {
+        // Copies issued at the start of phase t - 1 are first read in phase
+        // t + 1 and may stay in flight; everything older must have landed.
+        if (t > 0 && jb + (t - 1) / 2 + 1 <= je)
+          wait_vm<LPT>();
+        else
+          wait_vm<0>();
+        lds_barrier();
+        const int jn = jb + t / 2 + 1;
+        if (jn <= je) {
+          if ((t & 1) == 0)
+            issue_k(jn, ((jn - jb) & 1) ? sk1 : sk0);
+          else
+            issue_v(jn, ((jn - jb) & 1) ? sv1 : sv0);
+        }
+      };
+      if (grp == 1) phase_begin(0);
+      for (int i = 0; i < nt; ++i) {
+        f32x16 s[MB];
+        phase_begin(2 * i + grp);
+        scores((i & 1) ? sk1 : sk0, s);
+        publish(s);
+        phase_begin(2 * i + 1 + grp);
+        add_partner(s);
+        softmax_pv(jb + i, s, (i & 1) ? sv1 : sv0);
+      }
+      if (grp == 0) phase_begin(2 * nt);
     }
 
     if (jb != jlo_t || je != jhi_t) {
@@ -564,18 +628,33 @@ k_prefill(PrefillArgs a) {
         return reinterpret_cast<f32x4*>(a.part) + (((size_t)bh * a.npair + pair) * a.kpieces + pc) * 2 * slot_f4 +
                (size_t)seg * slot_f4;
       };
-      // Partials go through the device-coherent path (agent-scope relaxed
-      // atomics: stores write through the XCD's L2, loads do not trust it),
-      // so publishing them needs no L2-wide write-back or invalidation: wait
-      // for this work-group's stores, then bump the tile's counter.
-      float* mine = reinterpret_cast<float*>(slot_ptr(piece));
+      // Partials go through the device-coherent path (sc1: stores write
+      // through the XCD's L2 and loads do not trust it), so publishing them
+      // needs no L2-wide write-back or invalidation: wait for this
+      // work-group's stores, then bump the tile's counter.  Slot layout
+      // (bytes): accumulator quad (w * DBW + db, qd) of lane l at
+      // ((((w * DBW + db) * 4 + qd) * 64 + l) * 16), then m and l per (w, l).
+      constexpr unsigned kSlotBytes = (unsigned)(ACC_F4 * 16 + NW * 64 * 2 * 4);
+      constexpr int kSC1 = 16;  // cache-policy bit sc1 of the buffer instructions
+      auto slot_rsrc = [&](int pc) {
+        return __builtin_amdgcn_make_buffer_rsrc(slot_ptr(pc), 0, (int)kSlotBytes, 0x00020000);
+      };
+      const unsigned acc_off = (unsigned)((wave * DBW * 4 * 64 + lane) * 16);
+      const unsigned ml_off = (unsigned)(ACC_F4 * 16 + (wave * 64 + lane) * 4);
+      {
+        const auto r = slot_rsrc(piece);
 #pragma unroll
-      for (int db = 0; db < DBW; ++db)
-        global_store_sc1_f32x16(mine + ((size_t)(wave * DBW + db) * 4 * 64 + lane) * 4, acc[db]);
-      float* ml = mine + (size_t)ACC_F4 * 4;
-      __hip_atomic_store(ml + wave * 64 + lane, m_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ml + NW * 64 + wave * 64 + lane, l_i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // s_waitcnt: the stores above have landed
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, f32x4{acc[db][4 * qd], acc[db][4 * qd + 1], acc[db][4 * qd + 2],
+                                                acc[db][4 * qd + 3]}),
+                r, acc_off + (db * 4 + qd) * 1024, 0, kSC1);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_i), r, ml_off, 0, kSC1);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_i), r, ml_off + NW * 64 * 4, 0, kSC1);
+      }
+      wait_vm<0>();  // the stores above have landed
       __syncthreads();
       auto is_piece = [&](int pc) {
         const int x0 = ubound(pc), x1 = ubound(pc + 1);
@@ -599,30 +678,26 @@ k_prefill(PrefillArgs a) {
       float M = kNegInf;
       for (int pc = 0; pc < a.kpieces; ++pc)
         if (is_piece(pc))
-          M = fmaxf(M, __hip_atomic_load(reinterpret_cast<const float*>(slot_ptr(pc) + ACC_F4) + wave * 64 + lane,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(slot_rsrc(pc), ml_off, 0, kSC1)));
 #pragma unroll
       for (int db = 0; db < DBW; ++db) acc[db] = f32x16{};
       l_i = 0.f;
       for (int pc = 0; pc < a.kpieces; ++pc) {
         if (!is_piece(pc)) continue;
-        const float* src = reinterpret_cast<const float*>(slot_ptr(pc));
-        const float* sml = src + (size_t)ACC_F4 * 4;
-        const float mp = __hip_atomic_load(sml + wave * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float lp =
-            __hip_atomic_load(sml + NW * 64 + wave * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const auto r = slot_rsrc(pc);
+        const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ml_off, 0, kSC1));
+        const float lp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ml_off + NW * 64 * 4, 0, kSC1));
         const float f = mp == kNegInf ? 0.f : fast_exp2(mp - M);
         l_i += lp * f;
 #pragma unroll
         for (int db = 0; db < DBW; ++db)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, acc_off + (db * 4 + qd) * 1024, 0, kSC1));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[db][4 * qd + e] +=
-                  __hip_atomic_load(src + (((size_t)(wave * DBW + db) * 4 + qd) * 64 + lane) * 4 + e, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) *
-                  f;
+            for (int e = 0; e < 4; ++e) acc[db][4 * qd + e] += v[e] * f;
+          }
       }
       m_i = M;
     }
