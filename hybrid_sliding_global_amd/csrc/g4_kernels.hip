@@ -106,8 +106,12 @@ __device__ __forceinline__ void rope8(u32x4& x, u32x4& y, const double* rev, int
 // rows of a transpose-read group touch four disjoint chunk pairs.
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
 
-__device__ __forceinline__ void g2l16(const void* gsrc, void* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)ldst, 16, 0, 0);
+// Direct-to-LDS 16-byte load with the non-temporal cache policy, for data
+// read exactly once (the decode cache stream): it then neither evicts nor
+// competes with what L2 and the MALL hold, which lifts the streaming rate by
+// about a tenth.
+__device__ __forceinline__ void g2l16_nt(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)ldst, 16, 0, 2);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -854,8 +858,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
         const int byte = blk * 1024 + ln * 16;
         const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
         const int src_row = min(k0 + row, k_end - 1);
-        g2l16(base + (size_t)src_row * D + ((slot ^ swz(row)) << 3),
-              reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
+        g2l16_nt(base + (size_t)src_row * D + ((slot ^ swz(row)) << 3),
+                 reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
       }
     }
   };
