@@ -17,11 +17,12 @@ struct RopeRev {
 
 void fill_rope_rev(RopeRev* r, int head_dim, double theta);
 
-// Prefill tiling: key tile size per head size, query rows per work-group.
+// Prefill tiling: key tile size, query rows per work-group, and the number
+// of waves sharing one 32-row query group (head-dim split).  Both head sizes
+// use 32-key tiles and two waves per row group (eight waves, two per SIMD).
 constexpr int kPrefillRows = 128;
-inline int prefill_key_tile(int head_dim) { return head_dim == 512 ? 32 : 64; }
-// Waves sharing one 32-row query group (head-dim split) per head size.
-inline int prefill_dsplit(int head_dim) { return head_dim == 512 ? 2 : 1; }
+inline int prefill_key_tile(int /*head_dim*/) { return 32; }
+inline int prefill_dsplit(int /*head_dim*/) { return 2; }
 // Work-groups one prefill launch aims to keep busy: the CU count of an
 // MI355X (one resident prefill work-group per CU).  Fixed so that workspace
 // sizes can be computed without touching the device.

@@ -1175,10 +1175,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     hipLaunchKernelGGL((k_prefill<512, 32, 2>), grid_a, dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_prefill_prep<256, 64>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
+    hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
-    hipLaunchKernelGGL((k_prefill<256, 64, 1>), grid_a, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_prefill<256, 32, 2>), grid_a, dim3(512), 0, stream, a);
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   return hipGetLastError();

@@ -114,7 +114,7 @@ def _prefill_ws_model(B, S, Hq, Hkv, D, W):
     """Workspace layout of a prefill call: key and value operand images,
     arrival counters, partial-result slots of the query tiles split across
     work-groups."""
-    BN = 32 if D == 512 else 64
+    BN = 32
     ntiles = -(-S // BN)
     g = Hq // Hkv
     nqt = -(-(S * g) // 128)
@@ -135,7 +135,7 @@ def _prefill_ws_model(B, S, Hq, Hkv, D, W):
     img = -(-(B * Hkv * ntiles * BN * D * 2) // 256) * 256
     cnt = 2 * img
     part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256
-    nw = 8 if D == 512 else 4
+    nw = 8
     slot = 32 * D * 16 + nw * 64 * 2 * 4
     return part + (groups * k * 2 * slot if k > 1 else 0), k
 
