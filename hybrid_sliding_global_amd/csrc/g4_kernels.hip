@@ -679,6 +679,53 @@ k_prefill(PrefillArgs a) {
       // Deterministic merge: the result must not depend on which piece came
       // last, so every piece (this one re-read from its own slot) is added in
       // ascending piece order against the common maximum of all pieces.
+      // Two pieces (the common case) take a straight-line path with the same
+      // arithmetic whose loads are issued together instead of one round trip
+      // at a time.
+      int p0 = -1, p1 = -1;
+      for (int pc = 0; pc < a.kpieces; ++pc)
+        if (is_piece(pc)) {
+          if (p0 < 0)
+            p0 = pc;
+          else
+            p1 = pc;
+        }
+      if (npieces == 2) {
+        const auto r0 = slot_rsrc(p0), r1 = slot_rsrc(p1);
+        const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r0, ml_off, 0, kSC1));
+        const float l0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r0, ml_off + NW * 64 * 4, 0, kSC1));
+        const float m1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ml_off, 0, kSC1));
+        const float l1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ml_off + NW * 64 * 4, 0, kSC1));
+        const float M = fmaxf(fmaxf(kNegInf, m0), m1);
+        const float f0 = m0 == kNegInf ? 0.f : fast_exp2(m0 - M);
+        const float f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
+        l_i = 0.f;
+        l_i += l0 * f0;
+        l_i += l1 * f1;
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, acc_off + (db * 4 + qd) * 1024, 0, kSC1));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float t = 0.f;
+              t += v[e] * f0;
+              acc[db][4 * qd + e] = t;
+            }
+          }
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, acc_off + (db * 4 + qd) * 1024, 0, kSC1));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * qd + e] += v[e] * f1;
+          }
+        m_i = M;
+      } else {
       float M = kNegInf;
       for (int pc = 0; pc < a.kpieces; ++pc)
         if (is_piece(pc))
@@ -704,6 +751,7 @@ k_prefill(PrefillArgs a) {
           }
       }
       m_i = M;
+      }
     }
 
     const float l = l_i + __shfl_xor(l_i, 32);
