@@ -17,12 +17,14 @@ struct RopeRev {
 
 void fill_rope_rev(RopeRev* r, int head_dim, double theta);
 
-// Prefill tiling: key tile size, query rows per work-group, and the number
-// of waves sharing one 32-row query group (head-dim split).  Both head sizes
-// use 32-key tiles and two waves per row group (eight waves, two per SIMD).
+// Prefill tiling: 32-key tiles and 128 query rows per work-group for both
+// head sizes.  Head size 512 runs eight waves (two per SIMD, each pair of
+// waves splitting the head dimension of one 32-row group); head size 256
+// runs four waves (one per SIMD: scores by row block, output by head-dim
+// block).
 constexpr int kPrefillRows = 128;
 inline int prefill_key_tile(int /*head_dim*/) { return 32; }
-inline int prefill_dsplit(int /*head_dim*/) { return 2; }
+inline int prefill_waves(int head_dim) { return head_dim == 512 ? 8 : 4; }
 // Work-groups one prefill launch aims to keep busy: the CU count of an
 // MI355X (one resident prefill work-group per CU).  Fixed so that workspace
 // sizes can be computed without touching the device.

@@ -13,7 +13,10 @@
 //                     output as O^T += V^T P^T, so every per-query softmax
 //                     quantity lives in one lane (plus its partner 32 lanes
 //                     away).  For an aliased layer the value image is built
-//                     from the raw key cache.
+//                     from the raw key cache.  Head size 512 runs the
+//                     eight-wave k_prefill, head size 256 the four-wave
+//                     k_prefill4 (scores by row block, output by head-dim
+//                     block, P exchanged in bf16).
 // Decode = split-K over chunks of the visible key range:
 //   1. k_decode     : one work-group per (batch, kv-head, chunk); the four
 //                     waves split the head dimension, rotate keys on load,
@@ -30,6 +33,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "g4_internal.h"
 
@@ -50,6 +54,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr float kMaxGrowth = 64.f;     // log2 units: largest P = 2^(s - reference) the four-wave prefill allows
 #ifndef G4_PIPE_DEPTH
 #define G4_PIPE_DEPTH 4
 #endif
@@ -726,10 +731,20 @@ k_prefill(PrefillArgs a) {
           }
         m_i = M;
       } else {
+      // the pieces' maxima, eight loads per round trip
       float M = kNegInf;
-      for (int pc = 0; pc < a.kpieces; ++pc)
-        if (is_piece(pc))
-          M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(slot_rsrc(pc), ml_off, 0, kSC1)));
+      for (int pc0 = 0; pc0 < a.kpieces; pc0 += 8) {
+        float mv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int pc = pc0 + k;
+          mv[k] = (pc < a.kpieces && is_piece(pc))
+                      ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(slot_rsrc(pc), ml_off, 0, kSC1))
+                      : kNegInf;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) M = fmaxf(M, mv[k]);
+      }
 #pragma unroll
       for (int db = 0; db < DBW; ++db) acc[db] = f32x16{};
       l_i = 0.f;
@@ -773,6 +788,610 @@ k_prefill(PrefillArgs a) {
     if (u0 < nL) process(tl, 0, jlo_l + u0, jlo_l + min(u1, nL) - 1, jlo_l, jhi_l, 0, nL);
     if (u1 > nL) {
       if (u0 < nL) lds_barrier();  // the first segment's last tile may still be in use
+      process(ts, 1, jlo_s + max(u0, nL) - nL, jlo_s + u1 - nL - 1, jlo_s, jhi_s, nL, U);
+    }
+  }
+}
+
+// Score MFMAs of the four-wave prefill, written as asm so that their
+// accumulators stay in VGPRs: the compiler would otherwise put every MFMA
+// result of the kernel in AGPRs, where the output accumulators already take
+// all 256.  The first MFMA of a chain starts from zero; consecutive MFMAs
+// accumulating into the same registers need no wait states between them,
+// and the last one of a chain is followed by 24 wait states so that no
+// later instruction reads its result early (the compiler does not know
+// these are MFMAs and cannot insert them).
+__device__ __forceinline__ void mfma32v_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32v(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32v_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// Four-wave prefill, one wave per SIMD (register budget 512 per lane), for
+// one 128-row query tile of one (batch, kv-head) at a time; BN-key tiles.
+//
+//   scores : wave w owns query rows 32w .. 32w+31 over the whole head dim
+//            (queries rotated once into registers), so its S^T = K' Q'^T
+//            needs no exchange and its softmax statistics stay in the wave;
+//   output : wave w owns head-dim blocks [w*DBW, (w+1)*DBW) of all 128 rows,
+//            O^T += V^T P^T, with the four row blocks' P^T (bf16) and
+//            rescale factors exchanged through LDS.  Each value operand read
+//            from LDS then feeds four MFMAs.
+//
+// Software pipeline, one barrier per key tile: iteration i (key tile
+// jb + i) waits for the copies issued in iteration i-1, passes the barrier,
+// issues key tile i+1 and value tile i, computes S(i), then runs PV(i-1)
+// (whose P and rescale factors were published in iteration i-1) while the
+// softmax of S(i) runs, and publishes P(i).  Key tile i lives in key buffer
+// i&1 during iterations i-1 .. i, value tile i in value buffer i&1 during
+// iterations i .. i+1, P(i) in exchange buffer i&1 during i .. i+1.
+// The work split over work-groups (pairs of query tiles, pieces of their
+// key work) and the partial-result merge follow k_prefill.
+template <int D, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+k_prefill4(PrefillArgs a) {
+  constexpr int KSTEPS = D / 16;     // 32x32x16 steps over the head dim
+  constexpr int MB = BN / 32;        // 32-key blocks per tile
+  constexpr int KV = BN / 16;        // 16-key steps per tile
+  constexpr int DB = D / 32;         // 32-wide output blocks
+  constexpr int DBW = DB / 4;        // output blocks owned by one wave
+  constexpr int RB = 4;              // 32-row blocks per work-group (one per wave)
+  constexpr int TILE_BLKS = BN * D * 2 / 1024;
+  constexpr int LPT = TILE_BLKS / 4;  // 1 KiB blocks each wave copies per tile and operand
+  constexpr int ACC_F4 = 4 * RB * DBW * 4 * 64;  // f32x4 per partial slot (accumulators)
+  constexpr int kPipeDepth = G4_PIPE_DEPTH;
+  static_assert(LPT * 4 == TILE_BLKS, "tile must split evenly over the waves");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[2][BN * D];
+  __shared__ u32x4 sp[2][RB][KV][64];  // P^T operand of each row block, per 16-key step
+
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nblk = gridDim.x;
+  const int wid = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int per_bh = a.npair * a.kpieces;
+  const int bh = wid / per_bh, rem = wid % per_bh, pair = rem / a.kpieces, piece = rem % a.kpieces;
+  const int kvh = bh % a.Hkv, b = bh / a.Hkv;
+  const int rows_total = a.S * a.g;
+  const bool windowed = a.W > 0;
+
+  auto tile_keys = [&](int qt, int& jlo, int& jhi) {
+    const int r0 = qt * 128;
+    const int pmin = r0 / a.g, pmax = min(r0 + 127, rows_total - 1) / a.g;
+    jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
+    jhi = pmax / BN;
+  };
+  const int tl = a.nqt - 1 - pair;
+  const int ts = pair < tl ? pair : -1;
+  int jlo_l, jhi_l, jlo_s = 0, jhi_s = -1;
+  tile_keys(tl, jlo_l, jhi_l);
+  if (ts >= 0) tile_keys(ts, jlo_s, jhi_s);
+  const int nL = jhi_l - jlo_l + 1, nS = ts >= 0 ? jhi_s - jlo_s + 1 : 0, U = nL + nS;
+  auto ubound = [&](int j) { return (int)(((long long)j * U) / a.kpieces); };
+  const int u0 = ubound(piece), u1 = ubound(piece + 1);
+
+  const size_t slice_off = (size_t)(b * a.Hkv + kvh) * a.ntiles * (size_t)(BN * D);
+  const uint16_t* kimg = a.kimg + slice_off;
+  const uint16_t* vimg = a.vimg + slice_off;
+  const unsigned voff = (unsigned)(wave * 1024 + lane * 16);
+
+  auto issue_k = [&](int j, uint16_t* dk) {
+    const char* kt = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
+    const unsigned lk = lds_addr(dk) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) dma_block(kt + i * 4 * 1024, voff, lk + i * 4 * 1024);
+  };
+  auto issue_v = [&](int j, uint16_t* dv) {
+    const char* vt = reinterpret_cast<const char*>(vimg + (size_t)j * (BN * D));
+    const unsigned lv = lds_addr(dv) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) dma_block(vt + i * 4 * 1024, voff, lv + i * 4 * 1024);
+  };
+  // Block u (< LPT) of this wave's share of one operand tile.
+  auto issue_blk = [&](const uint16_t* img, int j, uint16_t* dst, int u) {
+    const char* src = reinterpret_cast<const char*>(img + (size_t)j * (BN * D));
+    dma_block(src + u * 4 * 1024, voff, lds_addr(dst) + wave * 1024 + u * 4 * 1024);
+  };
+
+  auto process = [&](int qt, int seg, int jb, int je, int jlo_t, int jhi_t, int us, int ue) __attribute__((always_inline)) {
+
+    const int r0 = qt * 128;
+    const int r = r0 + wave * 32 + n;
+    const int rc = r < rows_total ? r : rows_total - 1;
+    const int pos = rc / a.g;
+    const int pos_min = r0 / a.g;
+    const int pos_max = min(r0 + 127, rows_total - 1) / a.g;
+
+    // Q' = RoPE(q) * scale * log2(e) for this wave's rows, whole head dim:
+    // qf[ks] is the B operand of head-dim step ks (lane (n, h) holds elements
+    // 16 ks + 8 h + [0, 8)); rotation partners sit in steps ks and ks + KSTEPS/2.
+    bf16x8 qf[KSTEPS];
+    {
+      const int head = kvh * a.g + rc % a.g;
+      const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
+#pragma unroll
+      for (int i = 0; i < KSTEPS / 2; ++i) {
+        const int d0 = 16 * i + 8 * h;
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+        u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+        rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
+        qf[i] = as_bf16x8(x);
+        qf[i + KSTEPS / 2] = as_bf16x8(y);
+      }
+    }
+
+    f32x16 acc[RB][DBW];
+    float m_i, l_i;
+    float m_seen = kNegInf;  // largest score of this lane's row seen so far (log2 units)
+    float m_init = kNegInf;  // reference maximum a (re)started pass begins with
+    bool outgrown;           // some tile's maximum exceeded m_i + kMaxGrowth in this pass
+
+    // S^T for this wave's rows: s[mb] holds keys 32 mb + 8 i + 4 h + jj
+    // (register 4 i + jj) of query n.
+    // Operand reads run kPipeDepth MFMAs ahead; sched_barrier pins that order.
+    // step_hook(t) runs after MFMA t is issued (the tile copies ride there).
+    auto scores = [&](const uint16_t* ck, f32x16 (&s)[MB], auto&& after_first_reads, auto&& step_hook) {
+      const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + lane;
+      constexpr int N = MB * KSTEPS;  // step t: key block t % MB, head-dim step t / MB
+      u32x4 kr[kPipeDepth];
+#pragma unroll
+      for (int t = 0; t < kPipeDepth; ++t) kr[t] = kb[((t % MB) * KSTEPS + t / MB) * 64];
+      after_first_reads();
+#pragma unroll
+      for (int t = 0; t < N; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 kf = as_bf16x8(kr[t % kPipeDepth]);
+        if (t + kPipeDepth < N) {
+          const int u = t + kPipeDepth;
+          kr[t % kPipeDepth] = kb[((u % MB) * KSTEPS + u / MB) * 64];
+        }
+        const int mb = t % MB, ks = t / MB;
+        if (ks == 0)
+          mfma32v_first(s[mb], kf, qf[ks]);
+        else if (t >= N - MB && mb == MB - 1)
+          mfma32v_last(s[mb], kf, qf[ks]);
+        else
+          mfma32v(s[mb], kf, qf[ks]);
+        step_hook(t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Causal / window mask of key tile j; only tiles on the diagonal or at
+    // the window's lower edge need one.
+    auto needs_mask = [&](int j) {
+      const int kbase = j * BN;
+      return (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
+    };
+    auto mask = [&](int j, f32x16 (&s)[MB]) {
+      const int kbase = j * BN;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
+          const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+          s[mb][rr] = vis ? s[mb][rr] : kNegInf;
+        }
+    };
+
+    // Online softmax of one (masked) tile for this wave's rows.  Each row
+    // keeps one reference maximum m_i: the maximum of its first tile with a
+    // visible key.  Later tiles may exceed it by up to kMaxGrowth (P stays
+    // below 2^kMaxGrowth, far inside fp32 / bf16 range), so the accumulators
+    // are never rescaled inside the loop; a row that would exceed it marks
+    // the pass as outgrown and the work-group repeats the segment from a
+    // higher reference (see below).  P^T (bf16) goes to exchange buffer
+    // `buf`.  Branch-free, so it shares a scheduling region with the PV MFMAs.
+    auto softmax = [&](f32x16 (&s)[MB], int buf) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+      mx = max_lane_pair(mx);
+      m_seen = fmaxf(m_seen, mx);
+      m_i = (m_i == kNegInf) ? mx : m_i;  // nothing accumulated yet: adopt
+      outgrown |= mx > m_i + kMaxGrowth;
+      const float m_use = (m_i == kNegInf) ? 0.f : m_i;
+      float rs = 0.f;
+      unsigned pk[MB * 8];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) {
+          const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
+          rs += p0 + p1;
+          pk[mb * 8 + rr / 2] = pack_bf16(p0, p1);
+        }
+      l_i += rs;
+      // P^T slot t of key-step kv is key 16 kv + 4 h + t (t < 4) or
+      // 16 kv + 8 + 4 h + (t - 4): the order the value image stores V in.
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+        sp[buf][wave][kv][lane] = u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]};
+    };
+
+    // O^T += V^T P^T for one key tile over all four row blocks and this
+    // wave's head-dim blocks.  Operand blocks of key step kv: V (DBW blocks)
+    // and P^T (one per row block).
+    struct PvOps {
+      u32x4 v[DBW];
+      u32x4 p[RB];
+    };
+    auto load_ops = [&](const uint16_t* cv, int buf, int kv, PvOps& o) {
+      const u32x4* vb = reinterpret_cast<const u32x4*>(cv) + lane;
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) o.v[db] = vb[(kv * DB + wave * DBW + db) * 64];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o.p[rb] = sp[buf][rb][kv][lane];
+    };
+    auto pv = [&](const uint16_t* cv, int buf) {
+      PvOps o;
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+        load_ops(cv, buf, kv, o);
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma32(as_bf16x8(o.v[db]), as_bf16x8(o.p[rb]), acc[rb][db]);
+      }
+    };
+
+    // PV(i-1) with the softmax of S(i) woven in: PV MFMA t is followed by
+    // softmax stage t (row maximum; reference update; one pair of
+    // exponentials per stage; sum and P^T publication at the end), so the
+    // VALU work issues while the MFMAs run.  sched_barrier pins the order for
+    // the machine scheduler, and an empty asm that takes each stage's result
+    // keeps the IR optimisers from sinking the stage to its first use.  The operands of key step 0 arrive in `o0` (loaded during the
+    // score chain); those of step kv+1 are read at the start of step kv.
+    auto pv_softmax = [&](const uint16_t* cv, int pbuf, PvOps& o0, f32x16 (&s)[MB], int sbuf) {
+      constexpr int PER_KV = DBW * RB;
+      constexpr int NM = KV * PER_KV;
+      constexpr int NPAIR = MB * 8;
+      PvOps o1;
+      float mx = kNegInf, m_use = 0.f, rs = 0.f;
+      unsigned pk[MB * 8];
+#pragma unroll
+      for (int t = 0; t < NM; ++t) {
+        const int kv = t / PER_KV, db = (t / RB) % DBW, rb = t % RB;
+        PvOps& cur = (kv & 1) ? o1 : o0;
+        PvOps& nxt = (kv & 1) ? o0 : o1;
+        if (t % PER_KV == 0 && kv + 1 < KV) load_ops(cv, pbuf, kv + 1, nxt);
+        acc[rb][db] = mfma32(as_bf16x8(cur.v[db]), as_bf16x8(cur.p[rb]), acc[rb][db]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t == 0) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+          asm volatile("" : "+v"(mx));
+        } else if (t == 1) {
+          mx = max_lane_pair(mx);
+          m_seen = fmaxf(m_seen, mx);
+          m_i = (m_i == kNegInf) ? mx : m_i;  // nothing accumulated yet: adopt
+          outgrown |= mx > m_i + kMaxGrowth;
+          m_use = (m_i == kNegInf) ? 0.f : m_i;
+          asm volatile("" : "+v"(m_use));
+        } else if (t - 2 < NPAIR) {
+          const int k = t - 2, mb = k / 8, rr = 2 * (k % 8);
+          const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
+          rs += p0 + p1;
+          pk[k] = pack_bf16(p0, p1);
+          asm volatile("" : "+v"(pk[k]), "+v"(rs));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int k = NM - 2; k < NPAIR; ++k) {  // pairs left over when there are few MFMAs
+        const int mb = k / 8, rr = 2 * (k % 8);
+        const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
+        rs += p0 + p1;
+        pk[k] = pack_bf16(p0, p1);
+      }
+      l_i += rs;
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+        sp[sbuf][wave][kv][lane] = u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]};
+    };
+
+    // One pass over key tiles jb..je.  Returns false when a row of the
+    // work-group outgrew its reference maximum (the accumulated values are
+    // then unusable); the caller repeats the pass from the largest scores
+    // seen.  The pass always runs to its end, so the loop has a single exit.
+    const int nt = je - jb + 1;
+    auto pass = [&]() __attribute__((always_inline)) -> bool {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < DBW; ++i) acc[rb][i] = f32x16{};
+      m_i = m_init;
+      l_i = 0.f;
+      outgrown = false;
+      issue_k(jb, sk[0]);
+      wait_vm<0>();
+      lds_barrier();
+      if (1 < nt) issue_k(jb + 1, sk[1]);
+      issue_v(jb, sv[0]);
+      {
+        f32x16 s[MB];
+        scores(sk[0], s, [] {}, [](int) {});
+        if (needs_mask(jb)) mask(jb, s);
+        softmax(s, 0);
+      }
+      for (int i = 1; i < nt; ++i) {
+        wait_vm<0>();   // key tile i and value tile i-1 (issued one iteration ago) have landed
+        lds_barrier();  // ... for every wave; P(i-1) is published; buffers (i+1)&1 are free
+        const int pb = (i - 1) & 1;
+        f32x16 s[MB];
+        PvOps o0;
+        // The copies of key tile i+1 and value tile i are spread over the
+        // score chain, one per two MFMAs: issued back to back they would hold
+        // the wave (and with it the MFMA pipe) for hundreds of cycles.
+        const bool more = i + 1 < nt;
+        scores(sk[i & 1], s, [&] { load_ops(sv[pb], pb, 0, o0); }, [&](int t) {
+          if (t % 2 == 1 && t / 2 < 2 * LPT) {
+            const int u = t / 2;
+            if (u < LPT) {
+              if (more) issue_blk(kimg, jb + i + 1, sk[(i + 1) & 1], u);
+            } else {
+              issue_blk(vimg, jb + i, sv[i & 1], u - LPT);
+            }
+          }
+        });
+        static_assert(MB * KSTEPS >= 4 * LPT, "the score chain must be long enough to carry the copies");
+        if (needs_mask(jb + i)) mask(jb + i, s);
+        pv_softmax(sv[pb], pb, o0, s, i & 1);
+      }
+      wait_vm<0>();
+      lds_barrier();
+      const int pb = (nt - 1) & 1;
+      pv(sv[pb], pb);
+      // Work-group vote on `outgrown` (the flag words live in a key buffer,
+      // idle now that the last PV has read its operands).
+      int* vote = reinterpret_cast<int*>(&sk[1][0]);
+      const bool wave_outgrown = __builtin_amdgcn_ballot_w64(outgrown) != 0;  // all 64 lanes vote
+      if (lane == 0) vote[wave] = wave_outgrown;
+      lds_barrier();
+      const bool any = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+      lds_barrier();  // the words are read before anybody refills the buffer
+      return !any;
+    };
+    while (!pass()) {
+      // Nothing is in flight and every wave has passed the last barrier.
+      m_init = m_seen;
+    }
+
+    const size_t slot_f4 = (size_t)ACC_F4 + 4 * 64 / 2;
+    constexpr unsigned kSlotBytes = (unsigned)(ACC_F4 * 16 + 4 * 64 * 2 * 4);
+    constexpr int kSC1 = 16;
+    const unsigned acc_off = (unsigned)((wave * RB * DBW * 4 * 64 + lane) * 16);  // + ((rb * DBW + db) * 4 + qd) * 1024
+    auto ml_off = [&](int rb) { return (unsigned)(ACC_F4 * 16 + (rb * 64 + lane) * 4); };
+    // Output row of row block rb (query n of this lane), or null past the end.
+    auto out_row = [&](int rb) -> float* {
+      const int rr = r0 + 32 * rb + n;
+      if (rr >= rows_total) return nullptr;
+      const int p = rr / a.g, hd = kvh * a.g + rr % a.g;
+      return a.out + (((size_t)b * a.S + p) * a.Hq + hd) * D + 32 * wave * DBW;
+    };
+    if (jb != jlo_t || je != jhi_t) {
+      // Partial: store (O, m, l), then count this piece in (see k_prefill).
+      auto slot_rsrc = [&](int pc) {
+        f32x4* p = reinterpret_cast<f32x4*>(a.part) + (((size_t)bh * a.npair + pair) * a.kpieces + pc) * 2 * slot_f4 +
+                   (size_t)seg * slot_f4;
+        return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)kSlotBytes, 0x00020000);
+      };
+      {
+        const auto rs = slot_rsrc(piece);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int db = 0; db < DBW; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  __builtin_bit_cast(u32x4, f32x4{acc[rb][db][4 * qd], acc[rb][db][4 * qd + 1], acc[rb][db][4 * qd + 2],
+                                                  acc[rb][db][4 * qd + 3]}),
+                  rs, acc_off + ((rb * DBW + db) * 4 + qd) * 1024, 0, kSC1);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_i), rs, ml_off(wave), 0, kSC1);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_i), rs, ml_off(wave) + 4 * 64 * 4, 0, kSC1);
+      }
+      wait_vm<0>();
+      __syncthreads();
+      auto is_piece = [&](int pc) {
+        const int x0 = ubound(pc), x1 = ubound(pc + 1);
+        return x0 < x1 && x0 < ue && x1 > us;
+      };
+      // The pieces covering this tile in ascending order (empty pieces, which
+      // exist when there are more pieces than key tiles, are skipped, so the
+      // indices need not be consecutive); the first four are kept.
+      int npieces = 0, pcs[4] = {0, 0, 0, 0};
+      for (int pc = 0; pc < a.kpieces; ++pc)
+        if (is_piece(pc)) {
+          if (npieces < 4) pcs[npieces] = pc;
+          ++npieces;
+        }
+      const int p0 = pcs[0];
+      int* s_last = reinterpret_cast<int*>(&sk[0][0]);
+      if (tid == 0)
+        *s_last = __hip_atomic_fetch_add(&a.counters[(size_t)bh * a.nqt + qt], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+      __syncthreads();
+      const bool last = *s_last != 0;
+      __syncthreads();
+      if (!last) return;
+      // Deterministic merge in ascending piece order against the common
+      // maximum, written straight to the output: O = sum_k f_k O_k with
+      // f_k = 2^(m_k - M), accumulated as t = O_0 f_0, t = fma(O_k, f_k, t),
+      // whichever piece merges (every O_k, its own included, is read back
+      // from the slots).  A tile cut into NP <= 4 pieces is merged by
+      // straight-line code: one
+      // batch of (m, l) loads, then the accumulator chunks streamed a group
+      // (row block, head-dim block, half of its quads) at a time with the
+      // next group's loads in flight.
+      auto merge_np = [&](auto np_c) __attribute__((always_inline)) {
+        constexpr int NP = decltype(np_c)::value;
+        float f[NP][RB], inv[RB];
+        {
+          float mp[NP][RB], lp[NP][RB];
+#pragma unroll
+          for (int k = 0; k < NP; ++k) {
+            const auto rs = slot_rsrc(pcs[k]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              mp[k][rb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ml_off(rb), 0, kSC1));
+              lp[k][rb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ml_off(rb) + 4 * 64 * 4, 0, kSC1));
+            }
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            float M = mp[0][rb];
+#pragma unroll
+            for (int k = 1; k < NP; ++k) M = fmaxf(M, mp[k][rb]);
+            float lsum = 0.f;
+#pragma unroll
+            for (int k = 0; k < NP; ++k) {
+              f[k][rb] = mp[k][rb] == kNegInf ? 0.f : fast_exp2(mp[k][rb] - M);
+              lsum = k == 0 ? lp[0][rb] * f[0][rb] : __builtin_fmaf(lp[k][rb], f[k][rb], lsum);
+            }
+            const float lt = lsum + __shfl_xor(lsum, 32);
+            inv[rb] = lt > 0.f ? 1.f / lt : 0.f;
+          }
+        }
+        constexpr int NG = RB * DBW * 2;
+        f32x4 chunk[2][NP][2];
+        auto load_group = [&](int g, int sl) {
+          const int rb = g / (2 * DBW), db = (g / 2) % DBW, q0 = 2 * (g % 2);
+#pragma unroll
+          for (int k = 0; k < NP; ++k) {
+            const auto rs = slot_rsrc(pcs[k]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              chunk[sl][k][j] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, acc_off + ((rb * DBW + db) * 4 + q0 + j) * 1024, 0, kSC1));
+          }
+        };
+        load_group(0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (g + 1 < NG) load_group(g + 1, (g + 1) & 1);
+          const int rb = g / (2 * DBW), db = (g / 2) % DBW, q0 = 2 * (g % 2);
+          float* orow = out_row(rb);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int qd = q0 + j;
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float t = 0.f;
+#pragma unroll
+              for (int k = 0; k < NP; ++k) {
+                const float v = chunk[g & 1][k][j][e];
+                t = k == 0 ? v * f[0][rb] : __builtin_fmaf(v, f[k][rb], t);
+              }
+              o[e] = t * inv[rb];
+            }
+            if (orow) *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd + 4 * h) = o;
+          }
+        }
+      };
+      if (npieces == 2) {
+        merge_np(std::integral_constant<int, 2>{});
+      } else if (npieces == 3) {
+        merge_np(std::integral_constant<int, 3>{});
+      } else if (npieces == 4) {
+        merge_np(std::integral_constant<int, 4>{});
+      } else {
+        float M[RB], lsum[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) M[rb] = kNegInf, lsum[rb] = 0.f;
+        for (int pc = p0; pc < a.kpieces; ++pc)
+          if (is_piece(pc)) {
+            const auto rs = slot_rsrc(pc);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              M[rb] = fmaxf(M[rb], __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ml_off(rb), 0, kSC1)));
+          }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int db = 0; db < DBW; ++db) acc[rb][db] = f32x16{};
+        for (int pc = p0; pc < a.kpieces; ++pc) {
+          if (!is_piece(pc)) continue;
+          const auto rs = slot_rsrc(pc);
+          float f[RB];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ml_off(rb), 0, kSC1));
+            const float lp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ml_off(rb) + 4 * 64 * 4, 0, kSC1));
+            f[rb] = mp == kNegInf ? 0.f : fast_exp2(mp - M[rb]);
+            lsum[rb] = __builtin_fmaf(lp, f[rb], lsum[rb]);
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int db = 0; db < DBW; ++db)
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                const f32x4 v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, acc_off + ((rb * DBW + db) * 4 + qd) * 1024, 0, kSC1));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[rb][db][4 * qd + e] = __builtin_fmaf(v[e], f[rb], acc[rb][db][4 * qd + e]);
+              }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float lt = lsum[rb] + __shfl_xor(lsum[rb], 32);
+          const float inv = lt > 0.f ? 1.f / lt : 0.f;
+          float* orow = out_row(rb);
+          if (orow) {
+#pragma unroll
+            for (int db = 0; db < DBW; ++db)
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                f32x4 o = {acc[rb][db][4 * qd] * inv, acc[rb][db][4 * qd + 1] * inv, acc[rb][db][4 * qd + 2] * inv,
+                           acc[rb][db][4 * qd + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd + 4 * h) = o;
+              }
+          }
+        }
+      }
+      return;
+    }
+
+    // Whole tile here: the row blocks' denominators meet in LDS (the key
+    // buffers are idle once the last PV has started).
+    float* sl = reinterpret_cast<float*>(&sk[0][0]);
+    sl[wave * 64 + lane] = l_i + __shfl_xor(l_i, 32);
+    lds_barrier();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lt = sl[rb * 64 + lane];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* orow = out_row(rb);
+      if (orow) {
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 o = {acc[rb][db][4 * i] * inv, acc[rb][db][4 * i + 1] * inv, acc[rb][db][4 * i + 2] * inv,
+                       acc[rb][db][4 * i + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * h) = o;
+          }
+      }
+    }
+  };
+
+  if (u0 < u1) {
+    if (u0 < nL) process(tl, 0, jlo_l + u0, jlo_l + min(u1, nL) - 1, jlo_l, jhi_l, 0, nL);
+    if (u1 > nL) {
+      if (u0 < nL) lds_barrier();  // the first segment's buffers may still be in use
       process(ts, 1, jlo_s + max(u0, nL) - nL, jlo_s + u1 - nL - 1, jlo_s, jhi_s, nL, U);
     }
   }
@@ -1179,7 +1798,7 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   p.counters_off = p.vimg_off + (p.kimg_bytes + 255) / 256 * 256;
   p.ncounters = (size_t)B * Hkv * p.nqt;
   p.part_off = (p.counters_off + p.ncounters * 4 + 255) / 256 * 256;
-  const int nw = 4 * prefill_dsplit(D);
+  const int nw = prefill_waves(D);
   p.slot_bytes = (size_t)32 * D * 16 + (size_t)nw * 64 * 2 * 4;  // accumulators + (m, l) per wave and lane
   p.nslots = p.kpieces > 1 ? (size_t)groups * p.kpieces * 2 : 0;
   p.total = p.part_off + p.nslots * p.slot_bytes;
@@ -1226,7 +1845,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
     hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
-    hipLaunchKernelGGL((k_prefill<256, 32, 2>), grid_a, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((k_prefill4<256, 32>), grid_a, dim3(256), 0, stream, a);
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   return hipGetLastError();

@@ -135,7 +135,7 @@ def _prefill_ws_model(B, S, Hq, Hkv, D, W):
     img = -(-(B * Hkv * ntiles * BN * D * 2) // 256) * 256
     cnt = 2 * img
     part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256
-    nw = 8
+    nw = 8 if D == 512 else 4  # waves per work-group
     slot = 32 * D * 16 + nw * 64 * 2 * 4
     return part + (groups * k * 2 * slot if k > 1 else 0), k
 

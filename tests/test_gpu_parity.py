@@ -38,7 +38,10 @@ def _prefill_case(tag, B, S, Hq, Hkv, D, W, alias, Lmax=None, seed=0, rows=None,
         if v is not None:
             v[:, :, S:, :] = inputs.NAN_BF16
     st = Stack(layers)
-    out = st.prefill(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)])
+    # Workspace filled with 0xFF bytes (NaN as fp32): any read of a partial
+    # result slot that no work-group wrote in this call shows up as NaN.
+    ws = torch.full((st.prefill_workspace_bytes(0, B, S),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    out = st.prefill(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)], workspace=ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     want = oracle.prefill(q, k, v, W, theta, rows=rows)
