@@ -35,6 +35,7 @@ constexpr int kPrefillSlots = 256;
 // [partial-result slots]; each image is [B, Hkv, ntiles, BN * D] bf16.
 struct PrefillPlan {
   int BN = 0, ntiles = 0, g = 0, nqt = 0, npair = 0, kpieces = 0;
+  int paired = 1;  // work unit: 1 = query tiles t and nqt-1-t, 0 = one query tile
   size_t kimg_bytes = 0, vimg_off = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0,
          total = 0;
 };

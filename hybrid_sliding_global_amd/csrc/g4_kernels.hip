@@ -340,6 +340,7 @@ struct PrefillArgs {
   int* counters;  // [B * Hkv * nqt] arrival counts (zeroed by the key pass)
   float* part;    // partial-result slots
   int B, S, Hq, Hkv, g, Lmax, W, ntiles, nqt, npair, kpieces;
+  int paired;  // 1: work unit = query tiles t and nqt-1-t; 0: one query tile
   float qscale;  // softmax scale * log2(e): scores come out in log2 units
   RopeRev rope;
 };
@@ -408,8 +409,8 @@ k_prefill(PrefillArgs a) {
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = pmax / BN;
   };
-  const int tl = a.nqt - 1 - pair;       // long tile of the pair
-  const int ts = pair < tl ? pair : -1;  // short tile (none for the middle of an odd count)
+  const int tl = a.paired ? a.nqt - 1 - pair : pair;   // long tile of the pair
+  const int ts = a.paired && pair < tl ? pair : -1;   // short tile (none for the middle of an odd count)
   int jlo_l, jhi_l, jlo_s = 0, jhi_s = -1;
   tile_keys(tl, jlo_l, jhi_l);
   if (ts >= 0) tile_keys(ts, jlo_s, jhi_s);
@@ -846,8 +847,11 @@ k_prefill4(PrefillArgs a) {
   constexpr int kPipeDepth = G4_PIPE_DEPTH;
   static_assert(LPT * 4 == TILE_BLKS, "tile must split evenly over the waves");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[2][BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[2][BN * D];
+  // Key tiles kvb[0..1], value tiles kvb[2..3] (one block, so that the
+  // query-rotation table can borrow all of it before a segment starts).
+  __shared__ __attribute__((aligned(1024))) uint16_t kvb[4][BN * D];
+  uint16_t (*const sk)[BN * D] = kvb;
+  uint16_t (*const sv)[BN * D] = kvb + 2;
   __shared__ u32x4 sp[2][RB][KV][64];  // P^T operand of each row block, per 16-key step
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
@@ -867,8 +871,8 @@ k_prefill4(PrefillArgs a) {
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = pmax / BN;
   };
-  const int tl = a.nqt - 1 - pair;
-  const int ts = pair < tl ? pair : -1;
+  const int tl = a.paired ? a.nqt - 1 - pair : pair;
+  const int ts = a.paired && pair < tl ? pair : -1;
   int jlo_l, jhi_l, jlo_s = 0, jhi_s = -1;
   tile_keys(tl, jlo_l, jhi_l);
   if (ts >= 0) tile_keys(ts, jlo_s, jhi_s);
@@ -915,14 +919,63 @@ k_prefill4(PrefillArgs a) {
     {
       const int head = kvh * a.g + rc % a.g;
       const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
+      // The g query heads of a position share its rotation, so when the
+      // tile's positions fit, each (position, frequency) pair's cos / sin is
+      // computed once by the work-group into LDS (the idle tile buffers) and
+      // read back by every row of that position: the same values as
+      // computing them per row, at 1/g of the transcendental work.
+      constexpr int HF = D / 2;
+      const int npos = pos_max - pos_min + 1;
+      const bool shared_table = (size_t)npos * HF * sizeof(f32x2) <= sizeof(kvb);
+      if (shared_table) {
+        // this wave's query chunks are loaded first; their latency hides
+        // behind the table fill (rotated in place afterwards)
+        u32x4 xq[KSTEPS / 2], yq[KSTEPS / 2];
 #pragma unroll
-      for (int i = 0; i < KSTEPS / 2; ++i) {
-        const int d0 = 16 * i + 8 * h;
-        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
-        u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
-        rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
-        qf[i] = as_bf16x8(x);
-        qf[i + KSTEPS / 2] = as_bf16x8(y);
+        for (int i = 0; i < KSTEPS / 2; ++i) {
+          const int d0 = 16 * i + 8 * h;
+          xq[i] = *reinterpret_cast<const u32x4*>(qrow + d0);
+          yq[i] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+        }
+        // thread t fills frequency t % HF for every (256 / HF)-th position
+        f32x2* tab = reinterpret_cast<f32x2*>(&kvb[0][0]);
+        static_assert(256 % HF == 0, "frequencies must tile the work-group");
+        const int f = tid % HF;
+        const double rev = a.rope.rev[f];
+#pragma unroll 4
+        for (int pp = tid / HF; pp < npos; pp += 256 / HF) {
+          float sn, cs;
+          sincos_rev((double)(pos_min + pp), rev, sn, cs);
+          tab[pp * HF + f] = f32x2{cs, sn};
+        }
+        lds_barrier();
+        const f32x4* trow = reinterpret_cast<const f32x4*>(tab + (size_t)(pos - pos_min) * HF);
+#pragma unroll
+        for (int i = 0; i < KSTEPS / 2; ++i) {
+          const int d0 = 16 * i + 8 * h;
+          const u32x4 x = xq[i], y = yq[i];
+          u32x4 xo, yo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4 t = trow[d0 / 2 + e];  // (cos, sin) of frequencies d0 + 2e and d0 + 2e + 1
+            const float a0 = bf_lo(x[e]), a1 = bf_hi(x[e]), b0 = bf_lo(y[e]), b1 = bf_hi(y[e]);
+            xo[e] = pack_bf16((a0 * t[0] - b0 * t[1]) * a.qscale, (a1 * t[2] - b1 * t[3]) * a.qscale);
+            yo[e] = pack_bf16((b0 * t[0] + a0 * t[1]) * a.qscale, (b1 * t[2] + a1 * t[3]) * a.qscale);
+          }
+          qf[i] = as_bf16x8(xo);
+          qf[i + KSTEPS / 2] = as_bf16x8(yo);
+        }
+        lds_barrier();  // the table is read before the first tile copy lands on it
+      } else {
+#pragma unroll
+        for (int i = 0; i < KSTEPS / 2; ++i) {
+          const int d0 = 16 * i + 8 * h;
+          u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+          u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+          rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
+          qf[i] = as_bf16x8(x);
+          qf[i + KSTEPS / 2] = as_bf16x8(y);
+        }
       }
     }
 
@@ -1776,23 +1829,60 @@ static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int& jlo, int
   jhi = pmax / BN;
 }
 
+// Work split.  A work unit is either a pair of query tiles (t, nqt-1-t),
+// which evens out causal tiles, or a single query tile, which suits
+// windowed layers whose tiles all visit about the same number of key tiles;
+// each unit's key work is cut into kpieces ranges, one per work-group.
+// The choice minimises an estimate of the slowest work-group's time: key
+// tiles times the per-tile cost, plus a fixed cost per query-tile segment
+// (query load and rotation, first tile copy, output) and, when a tile is
+// split, the partial-result store and merge; the constants are per-kernel
+// cycle counts measured on MI355X.
+struct PrefillCosts {
+  double tile, segment, split;
+};
+static PrefillCosts prefill_costs(int D) {
+  if (D == 512) return {4700.0, 12000.0, 40000.0};
+  return {2400.0, 15000.0, 30000.0};
+}
+
 PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   PrefillPlan p;
   p.BN = prefill_key_tile(D);
   p.ntiles = ceil_div(S, p.BN);
   p.g = Hq / Hkv;
   p.nqt = ceil_div(S * p.g, kPrefillRows);
-  p.npair = (p.nqt + 1) / 2;
-  // largest key-work of a pair bounds the useful number of pieces
-  int umax = 1;
-  for (int i = 0; i < p.npair; ++i) {
-    int a0, a1, b0 = 0, b1 = -1;
-    prefill_tile_keys(p.nqt - 1 - i, S, p.g, W, p.BN, a0, a1);
-    if (i < p.nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, b0, b1);
-    umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
+  const PrefillCosts c = prefill_costs(D);
+  double best = 0.0;
+  for (int paired = 1; paired >= 0; --paired) {
+    const int nunits = paired ? (p.nqt + 1) / 2 : p.nqt;
+    // largest key work of a unit bounds the useful number of pieces
+    int umax = 1;
+    for (int i = 0; i < nunits; ++i) {
+      int a0, a1, b0 = 0, b1 = -1;
+      if (paired) {
+        prefill_tile_keys(p.nqt - 1 - i, S, p.g, W, p.BN, a0, a1);
+        if (i < p.nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, b0, b1);
+      } else {
+        prefill_tile_keys(i, S, p.g, W, p.BN, a0, a1);
+      }
+      umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
+    }
+    const long groups = (long)B * Hkv * nunits;
+    const int kmax = (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
+    for (int k = 1; k <= kmax; ++k) {
+      const double rounds = std::ceil((double)groups * k / kPrefillSlots);
+      const double segs = paired ? (k <= 2 ? 2.0 : 1.5) : 1.0;
+      const double t = rounds * (std::ceil((double)umax / k) * c.tile + segs * c.segment + (k > 1 ? c.split : 0.0));
+      if (best == 0.0 || t < best) {
+        best = t;
+        p.paired = paired;
+        p.npair = nunits;
+        p.kpieces = k;
+      }
+    }
   }
   const long groups = (long)B * Hkv * p.npair;
-  p.kpieces = (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
   p.kimg_bytes = (size_t)B * Hkv * p.ntiles * p.BN * D * 2;
   p.vimg_off = (p.kimg_bytes + 255) / 256 * 256;
   p.counters_off = p.vimg_off + (p.kimg_bytes + 255) / 256 * 256;
@@ -1827,6 +1917,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   a.ntiles = pl.ntiles;
   a.nqt = pl.nqt;
   a.npair = pl.npair;
+  a.paired = pl.paired;
   a.kpieces = pl.kpieces;
   a.qscale = p.scale * kLog2e;
   fill_rope_rev(&a.rope, p.D, p.theta);

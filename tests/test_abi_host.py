@@ -113,25 +113,39 @@ def test_kv_bytes_and_sharing(lib):
 def _prefill_ws_model(B, S, Hq, Hkv, D, W):
     """Workspace layout of a prefill call: key and value operand images,
     arrival counters, partial-result slots of the query tiles split across
-    work-groups."""
+    work-groups.  The work split is chosen by the same cost model as the
+    library (per-tile, per-segment and per-split cycle costs)."""
+    import math
     BN = 32
     ntiles = -(-S // BN)
     g = Hq // Hkv
     nqt = -(-(S * g) // 128)
-    npair = (nqt + 1) // 2
 
     def keys(qt):
         r0 = qt * 128
         pmin, pmax = r0 // g, min(r0 + 127, S * g - 1) // g
         return (max(0, pmin - W + 1) if W > 0 else 0) // BN, pmax // BN
 
-    umax = 1
-    for i in range(npair):
-        a0, a1 = keys(nqt - 1 - i)
-        b0, b1 = keys(i) if i < nqt - 1 - i else (0, -1)
-        umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
-    groups = B * Hkv * npair
-    k = max(1, min(256 // groups, umax, 64))
+    tile, segment, split = (4700.0, 12000.0, 40000.0) if D == 512 else (2400.0, 15000.0, 30000.0)
+    best = None
+    for paired in (1, 0):
+        nunits = (nqt + 1) // 2 if paired else nqt
+        umax = 1
+        for i in range(nunits):
+            if paired:
+                a0, a1 = keys(nqt - 1 - i)
+                b0, b1 = keys(i) if i < nqt - 1 - i else (0, -1)
+            else:
+                (a0, a1), (b0, b1) = keys(i), (0, -1)
+            umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
+        groups = B * Hkv * nunits
+        for k in range(1, max(1, min(256 // groups, umax, 64)) + 1):
+            rounds = math.ceil(groups * k / 256)
+            segs = (2.0 if k <= 2 else 1.5) if paired else 1.0
+            t = rounds * (math.ceil(umax / k) * tile + segs * segment + (split if k > 1 else 0.0))
+            if best is None or t < best[0]:
+                best = (t, groups, k)
+    _, groups, k = best
     img = -(-(B * Hkv * ntiles * BN * D * 2) // 256) * 256
     cnt = 2 * img
     part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256

@@ -75,6 +75,10 @@ def test_workload1_sliding_prefill_full_compare():
     (1, 129, 1, 1, 512, 0, False, 129),    # one head, one tile past a 128-row boundary
     (2, 96, 32, 2, 512, 0, False, 96),     # GQA group of 16
     (1, 300, 4, 4, 512, 64, True, 300),    # sliding layer with head size 512 (any kind/size pair works)
+    # causal layers long enough that query tiles are cut across work-groups
+    (1, 1024, 8, 1, 256, 0, False, 1024),  # single query tiles in up to 4 pieces
+    (1, 2048, 4, 1, 256, 0, False, 2048),  # pairs of query tiles in up to 8 pieces
+    (1, 640, 8, 2, 512, 0, False, 640),    # head size 512, pairs cut into 11 pieces
 ])
 def test_prefill_shapes(B, S, Hq, Hkv, D, W, alias, Lmax):
     _prefill_case("prefill B%d S%d Hq%d Hkv%d D%d W%d alias%d" % (B, S, Hq, Hkv, D, W, alias), B, S, Hq, Hkv, D, W,
