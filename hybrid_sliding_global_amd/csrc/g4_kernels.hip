@@ -246,7 +246,8 @@ __device__ __forceinline__ void lds_mfma_pipeline() {
 // --------------------------------------------------------- prefill: keys --
 
 // Direct-to-LDS copy of one 1 KiB block: lane l moves 16 bytes from
-// gbase + voff (voff = 16 * l + block offset) to LDS lds + 16 * l.  Written
+// gbase + voff (gbase: the tile, in SGPRs; voff = 16 * l + the block's
+// offset in the tile) to LDS lds + 16 * l.  Written
 // as asm on purpose: the compiler then does not see an LDS store, so it
 // schedules the plain LDS reads of the other buffer freely instead of
 // draining every outstanding copy (vmcnt(0)) in front of them.  The caller
@@ -256,6 +257,13 @@ __device__ __forceinline__ void lds_mfma_pipeline() {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsigned lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+// The same copy from a 64-bit per-lane address (VGPR pair), for kernels
+// whose scalar registers are too scarce to hold a tile base.
+__device__ __forceinline__ void dma_block_v(const void* gbase, unsigned voff, unsigned lds) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(gbase) + voff;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -428,13 +436,13 @@ k_prefill(PrefillArgs a) {
     const char* kt = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
     const unsigned lk = lds_addr(dk) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) dma_block(kt + i * NW * 1024, voff, lk + i * NW * 1024);
+    for (int i = 0; i < LPT; ++i) dma_block(kt, voff + i * NW * 1024, lk + i * NW * 1024);
   };
   auto issue_v = [&](int j, uint16_t* dv) {
     const char* vt = reinterpret_cast<const char*>(vimg + (size_t)j * (BN * D));
     const unsigned lv = lds_addr(dv) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) dma_block(vt + i * NW * 1024, voff, lv + i * NW * 1024);
+    for (int i = 0; i < LPT; ++i) dma_block(vt, voff + i * NW * 1024, lv + i * NW * 1024);
   };
   auto issue = [&](int j, uint16_t* dk, uint16_t* dv) {
     issue_k(j, dk);
@@ -885,22 +893,29 @@ k_prefill4(PrefillArgs a) {
   const uint16_t* vimg = a.vimg + slice_off;
   const unsigned voff = (unsigned)(wave * 1024 + lane * 16);
 
+  // Head size 512 leaves too few scalar registers for the tile bases.
+  auto copy_block = [&](const void* g, unsigned vo, unsigned l) {
+    if constexpr (D == 512)
+      dma_block_v(g, vo, l);
+    else
+      dma_block(g, vo, l);
+  };
   auto issue_k = [&](int j, uint16_t* dk) {
     const char* kt = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
     const unsigned lk = lds_addr(dk) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) dma_block(kt + i * 4 * 1024, voff, lk + i * 4 * 1024);
+    for (int i = 0; i < LPT; ++i) copy_block(kt, voff + i * 4 * 1024, lk + i * 4 * 1024);
   };
   auto issue_v = [&](int j, uint16_t* dv) {
     const char* vt = reinterpret_cast<const char*>(vimg + (size_t)j * (BN * D));
     const unsigned lv = lds_addr(dv) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) dma_block(vt + i * 4 * 1024, voff, lv + i * 4 * 1024);
+    for (int i = 0; i < LPT; ++i) copy_block(vt, voff + i * 4 * 1024, lv + i * 4 * 1024);
   };
   // Block u (< LPT) of this wave's share of one operand tile.
   auto issue_blk = [&](const uint16_t* img, int j, uint16_t* dst, int u) {
     const char* src = reinterpret_cast<const char*>(img + (size_t)j * (BN * D));
-    dma_block(src + u * 4 * 1024, voff, lds_addr(dst) + wave * 1024 + u * 4 * 1024);
+    copy_block(src, voff + u * 4 * 1024, lds_addr(dst) + wave * 1024 + u * 4 * 1024);
   };
 
   auto process = [&](int qt, int seg, int jb, int je, int jlo_t, int jhi_t, int us, int ue) __attribute__((always_inline)) {
@@ -1212,7 +1227,10 @@ k_prefill4(PrefillArgs a) {
       const bool wave_outgrown = __builtin_amdgcn_ballot_w64(outgrown) != 0;  // all 64 lanes vote
       if (lane == 0) vote[wave] = wave_outgrown;
       lds_barrier();
-      const bool any = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+      // (readfirstlane: the compiler cannot tell that an LDS read of one
+      // address is uniform, and a divergent loop exit would push the copy
+      // addresses out of scalar registers)
+      const bool any = __builtin_amdgcn_readfirstlane(vote[0] | vote[1] | vote[2] | vote[3]) != 0;
       lds_barrier();  // the words are read before anybody refills the buffer
       return !any;
     };
@@ -1276,7 +1294,7 @@ k_prefill4(PrefillArgs a) {
         *s_last = __hip_atomic_fetch_add(&a.counters[(size_t)bh * a.nqt + qt], 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
       __syncthreads();
-      const bool last = *s_last != 0;
+      const bool last = __builtin_amdgcn_readfirstlane(*s_last) != 0;
       __syncthreads();
       if (!last) return;
       // Deterministic merge in ascending piece order against the common
