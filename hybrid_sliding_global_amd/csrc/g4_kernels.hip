@@ -692,53 +692,79 @@ k_prefill(PrefillArgs a) {
       if (!last) return;
       // Deterministic merge: the result must not depend on which piece came
       // last, so every piece (this one re-read from its own slot) is added in
-      // ascending piece order against the common maximum of all pieces.
-      // Two pieces (the common case) take a straight-line path with the same
-      // arithmetic whose loads are issued together instead of one round trip
-      // at a time.
-      int p0 = -1, p1 = -1;
+      // ascending piece order against the common maximum of all pieces:
+      // t = O_0 f_0, t = fma(O_k, f_k, t).  A tile cut into at most four
+      // pieces is merged by straight-line code (one batch of (m, l) loads,
+      // then the accumulator chunks streamed with the next chunk's loads in
+      // flight); the pieces' indices need not be consecutive (empty pieces
+      // are skipped).
+      int pcs[4] = {0, 0, 0, 0}, nfound = 0;
       for (int pc = 0; pc < a.kpieces; ++pc)
         if (is_piece(pc)) {
-          if (p0 < 0)
-            p0 = pc;
-          else
-            p1 = pc;
+          if (nfound < 4) pcs[nfound] = pc;
+          ++nfound;
         }
-      if (npieces == 2) {
-        const auto r0 = slot_rsrc(p0), r1 = slot_rsrc(p1);
-        const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r0, ml_off, 0, kSC1));
-        const float l0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r0, ml_off + NW * 64 * 4, 0, kSC1));
-        const float m1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ml_off, 0, kSC1));
-        const float l1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ml_off + NW * 64 * 4, 0, kSC1));
-        const float M = fmaxf(fmaxf(kNegInf, m0), m1);
-        const float f0 = m0 == kNegInf ? 0.f : fast_exp2(m0 - M);
-        const float f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
-        l_i = 0.f;
-        l_i += l0 * f0;
-        l_i += l1 * f1;
+      auto merge_np = [&](auto np_c) __attribute__((always_inline)) {
+        constexpr int NP = decltype(np_c)::value;
+        float f[NP];
+        {
+          float mp[NP], lp[NP];
 #pragma unroll
-        for (int db = 0; db < DBW; ++db)
+          for (int k = 0; k < NP; ++k) {
+            const auto r = slot_rsrc(pcs[k]);
+            mp[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ml_off, 0, kSC1));
+            lp[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ml_off + NW * 64 * 4, 0, kSC1));
+          }
+          float M = mp[0];
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 v = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, acc_off + (db * 4 + qd) * 1024, 0, kSC1));
+          for (int k = 1; k < NP; ++k) M = fmaxf(M, mp[k]);
+          float lsum = 0.f;
+#pragma unroll
+          for (int k = 0; k < NP; ++k) {
+            f[k] = mp[k] == kNegInf ? 0.f : fast_exp2(mp[k] - M);
+            lsum = k == 0 ? lp[0] * f[0] : __builtin_fmaf(lp[k], f[k], lsum);
+          }
+          l_i = lsum;
+          m_i = M;
+        }
+        constexpr int NG = DBW * 2;  // (head-dim block, half of its quads)
+        f32x4 chunk[2][NP][2];
+        auto load_group = [&](int g, int sl) {
+          const int db = g / 2, q0 = 2 * (g % 2);
+#pragma unroll
+          for (int k = 0; k < NP; ++k) {
+            const auto r = slot_rsrc(pcs[k]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              chunk[sl][k][j] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, acc_off + (db * 4 + q0 + j) * 1024, 0, kSC1));
+          }
+        };
+        load_group(0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (g + 1 < NG) load_group(g + 1, (g + 1) & 1);
+          const int db = g / 2, q0 = 2 * (g % 2);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float t = 0.f;
-              t += v[e] * f0;
-              acc[db][4 * qd + e] = t;
+#pragma unroll
+              for (int k = 0; k < NP; ++k) {
+                const float v = chunk[g & 1][k][j][e];
+                t = k == 0 ? v * f[0] : __builtin_fmaf(v, f[k], t);
+              }
+              acc[db][4 * (q0 + j) + e] = t;
             }
-          }
-#pragma unroll
-        for (int db = 0; db < DBW; ++db)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 v = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, acc_off + (db * 4 + qd) * 1024, 0, kSC1));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[db][4 * qd + e] += v[e] * f1;
-          }
-        m_i = M;
+        }
+      };
+      if (npieces == 2) {
+        merge_np(std::integral_constant<int, 2>{});
+      } else if (npieces == 3) {
+        merge_np(std::integral_constant<int, 3>{});
+      } else if (npieces == 4) {
+        merge_np(std::integral_constant<int, 4>{});
       } else {
       // the pieces' maxima, eight loads per round trip
       float M = kNegInf;
