@@ -283,6 +283,11 @@ __device__ __forceinline__ void dma_block_v(const void* gbase, unsigned voff, un
 // Values are not rotated (for an aliased layer `v` is the raw key buffer).
 // Rows at or beyond S are written as zeros.  Also clears the attention
 // kernel's arrival counters (this launch precedes it on the same stream).
+//
+// Grid (2 * ntiles, Hkv, B): even work-groups write a tile's key image, odd
+// ones its value image.  Every thread issues all of its global loads before
+// it uses any of them, so a work-group costs one memory round trip rather
+// than one per loop step.
 template <int D, int BN>
 __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                       uint16_t* __restrict__ kimg, uint16_t* __restrict__ vimg, int S,
@@ -290,42 +295,67 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict
                                                       int ncounters) {
   constexpr int KSTEPS = D / 16, DB = D / 32, KV = BN / 16;
   constexpr int PITCH = D + 8;  // staged value row, bf16 elements (16-byte skew per row)
+  constexpr int CH = D / 16;    // 16-byte chunks per half key row
+  constexpr int NK = BN * CH / 256, NV = BN * (D / 8) / 256, NG = KV * DB * 64 / 256;
+  static_assert(NK * 256 == BN * CH && NV * 256 == BN * (D / 8) && NG * 256 == KV * DB * 64, "tile split");
   __shared__ __attribute__((aligned(16))) uint16_t sv[BN * PITCH];
-  const int t = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int t = blockIdx.x >> 1, kvh = blockIdx.y, b = blockIdx.z;
   const int flat = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
   for (int i = flat * 256 + threadIdx.x; i < ncounters; i += gridDim.x * gridDim.y * gridDim.z * 256) counters[i] = 0;
   const size_t slice = ((size_t)b * Hkv + kvh) * (size_t)Lmax * D;
   const size_t tile = (((size_t)b * Hkv + kvh) * ntiles + t) * (size_t)(BN * D);
-  const uint16_t* ksrc = k + slice;
-  const uint16_t* vsrc = v + slice;
-  uint16_t* kdst = kimg + tile;
-  uint16_t* vdst = vimg + tile;
 
-  // keys: chunk c (8 elements at 8c) of the first half pairs with chunk c of the second half
-  constexpr int CH = D / 16;
-  for (int it = threadIdx.x; it < BN * CH; it += 256) {
-    const int row = it / CH, c = it % CH, p = t * BN + row;
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (p < S) {
-      const uint16_t* r = ksrc + (size_t)p * D;
-      x = *reinterpret_cast<const u32x4*>(r + 8 * c);
-      y = *reinterpret_cast<const u32x4*>(r + D / 2 + 8 * c);
-      rope8(x, y, rope.rev, 8 * c, (double)p, 1.0f);
+  if ((blockIdx.x & 1) == 0) {
+    // keys: chunk c (8 elements at 8c) of the first half pairs with chunk c of
+    // the second half; a thread keeps one chunk index c for all its rows
+    static_assert(256 % CH == 0, "chunk index fixed per thread");
+    const uint16_t* ksrc = k + slice;
+    uint16_t* kdst = kimg + tile;
+    const int c = threadIdx.x % CH, row0 = threadIdx.x / CH;
+    u32x4 x[NK], y[NK];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int p = t * BN + row0 + j * (256 / CH);
+      const uint16_t* r = ksrc + (size_t)min(p, S - 1) * D;  // rows past S load row S-1, then become zeros
+      x[j] = *reinterpret_cast<const u32x4*>(r + 8 * c);
+      y[j] = *reinterpret_cast<const u32x4*>(r + D / 2 + 8 * c);
     }
-    const int lane = (row & 31) + 32 * (c & 1), mb = row >> 5;
-    *reinterpret_cast<u32x4*>(kdst + ((mb * KSTEPS + (c >> 1)) * 64 + lane) * 8) = x;
-    *reinterpret_cast<u32x4*>(kdst + ((mb * KSTEPS + KSTEPS / 2 + (c >> 1)) * 64 + lane) * 8) = y;
+    double rev[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rev[e] = rope.rev[8 * c + e];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int row = row0 + j * (256 / CH), p = t * BN + row;
+      rope8(x[j], y[j], rev, 0, (double)p, 1.0f);
+      if (p >= S) {
+        x[j] = u32x4{0, 0, 0, 0};
+        y[j] = u32x4{0, 0, 0, 0};
+      }
+      const int lane = (row & 31) + 32 * (c & 1), mb = row >> 5;
+      *reinterpret_cast<u32x4*>(kdst + ((mb * KSTEPS + (c >> 1)) * 64 + lane) * 8) = x[j];
+      *reinterpret_cast<u32x4*>(kdst + ((mb * KSTEPS + KSTEPS / 2 + (c >> 1)) * 64 + lane) * 8) = y[j];
+    }
+    return;
   }
 
   // values: stage the tile's rows, then gather the transposed lane slots
-  for (int it = threadIdx.x; it < BN * (D / 8); it += 256) {
-    const int row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
-    u32x4 x = {0, 0, 0, 0};
-    if (p < S) x = *reinterpret_cast<const u32x4*>(vsrc + (size_t)p * D + 8 * c);
-    *reinterpret_cast<u32x4*>(sv + row * PITCH + 8 * c) = x;
+  const uint16_t* vsrc = v + slice;
+  uint16_t* vdst = vimg + tile;
+  u32x4 x[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int it = threadIdx.x + 256 * j, row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
+    x[j] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)min(p, S - 1) * D + 8 * c);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int it = threadIdx.x + 256 * j, row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
+    *reinterpret_cast<u32x4*>(sv + row * PITCH + 8 * c) = p < S ? x[j] : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  for (int it = threadIdx.x; it < KV * DB * 64; it += 256) {
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int it = threadIdx.x + 256 * j;
     const int lane = it & 63, blk = it >> 6, kv = blk / DB, db = blk % DB;
     const int d = 32 * db + (lane & 31), k0 = 16 * kv + 4 * (lane >> 5);
     u32x4 o;
@@ -1965,7 +1995,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   a.kpieces = pl.kpieces;
   a.qscale = p.scale * kLog2e;
   fill_rope_rev(&a.rope, p.D, p.theta);
-  const dim3 grid_k(pl.ntiles, p.Hkv, p.B);
+  const dim3 grid_k(2 * pl.ntiles, p.Hkv, p.B);
   const dim3 grid_a((unsigned)((long)p.B * p.Hkv * pl.npair * pl.kpieces));
   const uint16_t* kraw = static_cast<const uint16_t*>(p.k);
   const uint16_t* vraw = static_cast<const uint16_t*>(p.v);
