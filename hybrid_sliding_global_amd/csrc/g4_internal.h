@@ -18,7 +18,7 @@ struct RopeRev {
 void fill_rope_rev(RopeRev* r, int head_dim, double theta);
 
 // Prefill tiling: 32-key tiles and 128 query rows per work-group for both
-// head sizes.  Head size 512 runs eight waves (two per SIMD, each pair of
+// head sizes (head size 256 may instead run 64-row tiles).  Head size 512 runs eight waves (two per SIMD, each pair of
 // waves splitting the head dimension of one 32-row group); head size 256
 // runs four waves (one per SIMD: scores by row block, output by head-dim
 // block).
@@ -35,6 +35,7 @@ constexpr int kPrefillSlots = 256;
 // [partial-result slots]; each image is [B, Hkv, ntiles, BN * D] bf16.
 struct PrefillPlan {
   int BN = 0, ntiles = 0, g = 0, nqt = 0, npair = 0, kpieces = 0;
+  int rows = kPrefillRows;  // query rows per tile: 128, or 64 (head size 256, never cut into pieces)
   int paired = 1;  // work unit: 1 = query tiles t and nqt-1-t, 0 = one query tile
   size_t kimg_bytes = 0, vimg_off = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0,
          total = 0;

@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <type_traits>
 
@@ -875,6 +876,17 @@ __device__ __forceinline__ void mfma32v(f32x16& d, const bf16x8& a, const bf16x8
 __device__ __forceinline__ void mfma32v_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d) : "v"(a), "v"(b));
 }
+// The same for the 16x16x32 score chains of 64-row tiles (two chains,
+// interleaved; the wait states after the last MFMA cover both).
+__device__ __forceinline__ void mfma16v_first(f32x4& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16v(f32x4& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16v_last(f32x4& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d) : "v"(a), "v"(b));
+}
 
 // Four-wave prefill, one wave per SIMD (register budget 512 per lane), for
 // one 128-row query tile of one (batch, kv-head) at a time; BN-key tiles.
@@ -896,29 +908,38 @@ __device__ __forceinline__ void mfma32v_last(f32x16& d, const bf16x8& a, const b
 // iterations i .. i+1, P(i) in exchange buffer i&1 during i .. i+1.
 // The work split over work-groups (pairs of query tiles, pieces of their
 // key work) and the partial-result merge follow k_prefill.
-template <int D, int BN>
+template <int D, int BN, int ROWS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 k_prefill4(PrefillArgs a) {
+  static_assert(ROWS == 128 || ROWS == 64, "query tile of 128 or 64 rows");
+  constexpr bool R64 = ROWS == 64;   // 16 score rows per wave (16x16x32 MFMAs), no split pieces
   constexpr int KSTEPS = D / 16;     // 32x32x16 steps over the head dim
   constexpr int MB = BN / 32;        // 32-key blocks per tile
   constexpr int KV = BN / 16;        // 16-key steps per tile
   constexpr int DB = D / 32;         // 32-wide output blocks
   constexpr int DBW = DB / 4;        // output blocks owned by one wave
-  constexpr int RB = 4;              // 32-row blocks per work-group (one per wave)
+  constexpr int RB = ROWS / 32;      // 32-row blocks of the output MFMAs
+  constexpr int SR = ROWS / 4;       // query rows whose scores one wave computes
+  constexpr int NQ = R64 ? D / 64 : D / 32;  // (d, d + D/2) query chunk pairs per lane
+  static_assert(!R64 || BN == 32, "64-row tiles use 32-key tiles");
   constexpr int TILE_BLKS = BN * D * 2 / 1024;
   constexpr int LPT = TILE_BLKS / 4;  // 1 KiB blocks each wave copies per tile and operand
   constexpr int ACC_F4 = 4 * RB * DBW * 4 * 64;  // f32x4 per partial slot (accumulators)
   constexpr int kPipeDepth = G4_PIPE_DEPTH;
   static_assert(LPT * 4 == TILE_BLKS, "tile must split evenly over the waves");
 
-  // Key tiles kvb[0..1], value tiles kvb[2..3] (one block, so that the
-  // query-rotation table can borrow all of it before a segment starts).
+  // Key tiles kvb[0..1], value tiles kvb[2..3].
   __shared__ __attribute__((aligned(1024))) uint16_t kvb[4][BN * D];
   uint16_t (*const sk)[BN * D] = kvb;
   uint16_t (*const sv)[BN * D] = kvb + 2;
   __shared__ u32x4 sp[2][RB][KV][64];  // P^T operand of each row block, per 16-key step
+  // Query-rotation table (cos, sin) per (position, frequency) of a segment;
+  // a region of its own, so that a segment's first tile copies are already
+  // in flight while its queries are rotated.
+  __shared__ __attribute__((aligned(16))) f32x2 rtab[65536 / sizeof(f32x2)];
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int j16 = lane & 15, grp = lane >> 4;  // 64-row tiles: score lane = (row j16, key group grp)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int nblk = gridDim.x;
@@ -930,8 +951,8 @@ k_prefill4(PrefillArgs a) {
   const bool windowed = a.W > 0;
 
   auto tile_keys = [&](int qt, int& jlo, int& jhi) {
-    const int r0 = qt * 128;
-    const int pmin = r0 / a.g, pmax = min(r0 + 127, rows_total - 1) / a.g;
+    const int r0 = qt * ROWS;
+    const int pmin = r0 / a.g, pmax = min(r0 + ROWS - 1, rows_total - 1) / a.g;
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = pmax / BN;
   };
@@ -976,17 +997,30 @@ k_prefill4(PrefillArgs a) {
 
   auto process = [&](int qt, int seg, int jb, int je, int jlo_t, int jhi_t, int us, int ue) __attribute__((always_inline)) {
 
-    const int r0 = qt * 128;
-    const int r = r0 + wave * 32 + n;
+    const int r0 = qt * ROWS;
+    const int r = r0 + wave * SR + (R64 ? j16 : n);  // this lane's score row
     const int rc = r < rows_total ? r : rows_total - 1;
     const int pos = rc / a.g;
     const int pos_min = r0 / a.g;
-    const int pos_max = min(r0 + 127, rows_total - 1) / a.g;
+    const int pos_max = min(r0 + ROWS - 1, rows_total - 1) / a.g;
+    const int nt = je - jb + 1;
+
+    // The first two key tiles and the first value tile of a pass, issued
+    // together: one memory round trip instead of two.
+    auto issue_head = [&]() __attribute__((always_inline)) {
+      issue_k(jb, sk[0]);
+      issue_v(jb, sv[0]);
+      if (1 < nt) issue_k(jb + 1, sk[1]);
+    };
+    issue_head();  // lands while the queries are loaded and rotated
 
     // Q' = RoPE(q) * scale * log2(e) for this wave's rows, whole head dim:
-    // qf[ks] is the B operand of head-dim step ks (lane (n, h) holds elements
-    // 16 ks + 8 h + [0, 8)); rotation partners sit in steps ks and ks + KSTEPS/2.
-    bf16x8 qf[KSTEPS];
+    // qf[ks] is the B operand of head-dim step ks.  128-row tiles (32x32x16
+    // steps): lane (n, h) holds elements 16 ks + 8 h + [0, 8).  64-row tiles
+    // (16x16x32 steps): lane (j16, grp) holds elements 32 ks + 8 grp + [0, 8).
+    // Rotation partners sit in steps ks and ks + NQ.
+    bf16x8 qf[2 * NQ];
+    auto qchunk = [&](int i) { return R64 ? 32 * i + 8 * grp : 16 * i + 8 * h; };
     {
       const int head = kvh * a.g + rc % a.g;
       const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
@@ -997,19 +1031,19 @@ k_prefill4(PrefillArgs a) {
       // computing them per row, at 1/g of the transcendental work.
       constexpr int HF = D / 2;
       const int npos = pos_max - pos_min + 1;
-      const bool shared_table = (size_t)npos * HF * sizeof(f32x2) <= sizeof(kvb);
+      const bool shared_table = (size_t)npos * HF * sizeof(f32x2) <= sizeof(rtab);
       if (shared_table) {
         // this wave's query chunks are loaded first; their latency hides
         // behind the table fill (rotated in place afterwards)
-        u32x4 xq[KSTEPS / 2], yq[KSTEPS / 2];
+        u32x4 xq[NQ], yq[NQ];
 #pragma unroll
-        for (int i = 0; i < KSTEPS / 2; ++i) {
-          const int d0 = 16 * i + 8 * h;
+        for (int i = 0; i < NQ; ++i) {
+          const int d0 = qchunk(i);
           xq[i] = *reinterpret_cast<const u32x4*>(qrow + d0);
           yq[i] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
         }
         // thread t fills frequency t % HF for every (256 / HF)-th position
-        f32x2* tab = reinterpret_cast<f32x2*>(&kvb[0][0]);
+        f32x2* tab = rtab;
         static_assert(256 % HF == 0, "frequencies must tile the work-group");
         const int f = tid % HF;
         const double rev = a.rope.rev[f];
@@ -1022,8 +1056,8 @@ k_prefill4(PrefillArgs a) {
         lds_barrier();
         const f32x4* trow = reinterpret_cast<const f32x4*>(tab + (size_t)(pos - pos_min) * HF);
 #pragma unroll
-        for (int i = 0; i < KSTEPS / 2; ++i) {
-          const int d0 = 16 * i + 8 * h;
+        for (int i = 0; i < NQ; ++i) {
+          const int d0 = qchunk(i);
           const u32x4 x = xq[i], y = yq[i];
           u32x4 xo, yo;
 #pragma unroll
@@ -1034,57 +1068,86 @@ k_prefill4(PrefillArgs a) {
             yo[e] = pack_bf16((b0 * t[0] + a0 * t[1]) * a.qscale, (b1 * t[2] + a1 * t[3]) * a.qscale);
           }
           qf[i] = as_bf16x8(xo);
-          qf[i + KSTEPS / 2] = as_bf16x8(yo);
+          qf[i + NQ] = as_bf16x8(yo);
         }
-        lds_barrier();  // the table is read before the first tile copy lands on it
       } else {
 #pragma unroll
-        for (int i = 0; i < KSTEPS / 2; ++i) {
-          const int d0 = 16 * i + 8 * h;
+        for (int i = 0; i < NQ; ++i) {
+          const int d0 = qchunk(i);
           u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
           u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
           rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
           qf[i] = as_bf16x8(x);
-          qf[i + KSTEPS / 2] = as_bf16x8(y);
+          qf[i + NQ] = as_bf16x8(y);
         }
       }
     }
 
     f32x16 acc[RB][DBW];
+    // Scores of one key tile for this wave's rows (layout: see scores()).
+    using SArr = std::conditional_t<R64, f32x4[2], f32x16[MB]>;
     float m_i, l_i;
     float m_seen = kNegInf;  // largest score of this lane's row seen so far (log2 units)
     float m_init = kNegInf;  // reference maximum a (re)started pass begins with
     bool outgrown;           // some tile's maximum exceeded m_i + kMaxGrowth in this pass
 
-    // S^T for this wave's rows: s[mb] holds keys 32 mb + 8 i + 4 h + jj
-    // (register 4 i + jj) of query n.
+    // S^T for this wave's rows.  128-row tiles: s[mb] holds keys
+    // 32 mb + 8 i + 4 h + jj (register 4 i + jj) of query n.  64-row tiles:
+    // s[mb] holds keys 16 mb + 4 grp + ii (register ii) of query j16.
     // Operand reads run kPipeDepth MFMAs ahead; sched_barrier pins that order.
     // step_hook(t) runs after MFMA t is issued (the tile copies ride there).
-    auto scores = [&](const uint16_t* ck, f32x16 (&s)[MB], auto&& after_first_reads, auto&& step_hook) {
-      const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + lane;
-      constexpr int N = MB * KSTEPS;  // step t: key block t % MB, head-dim step t / MB
-      u32x4 kr[kPipeDepth];
+    auto scores = [&](const uint16_t* ck, SArr& s, auto&& after_first_reads, auto&& step_hook) {
+      if constexpr (R64) {
+        // 16x16x32 steps: lane (j16, grp) takes key 16 mb + j16, head dims
+        // 32 ks + 8 grp + [0, 8): half (grp & 1) of lane slot 16 mb + j16 in
+        // key-image block 2 ks + (grp >> 1).
+        const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + ((grp >> 1) * 64 + j16 + 32 * (grp & 1));
+        constexpr int N = 2 * (D / 32);  // step t: key block t % 2, head-dim step t / 2
+        auto kaddr = [](int t) { return 2 * (t / 2) * 64 + 16 * (t % 2); };
+        u32x4 kr[kPipeDepth];
 #pragma unroll
-      for (int t = 0; t < kPipeDepth; ++t) kr[t] = kb[((t % MB) * KSTEPS + t / MB) * 64];
-      after_first_reads();
+        for (int t = 0; t < kPipeDepth; ++t) kr[t] = kb[kaddr(t)];
+        after_first_reads();
 #pragma unroll
-      for (int t = 0; t < N; ++t) {
-        __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 kf = as_bf16x8(kr[t % kPipeDepth]);
-        if (t + kPipeDepth < N) {
-          const int u = t + kPipeDepth;
-          kr[t % kPipeDepth] = kb[((u % MB) * KSTEPS + u / MB) * 64];
+        for (int t = 0; t < N; ++t) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 kf = as_bf16x8(kr[t % kPipeDepth]);
+          if (t + kPipeDepth < N) kr[t % kPipeDepth] = kb[kaddr(t + kPipeDepth)];
+          if (t < 2)
+            mfma16v_first(s[t % 2], kf, qf[t / 2]);
+          else if (t == N - 1)
+            mfma16v_last(s[t % 2], kf, qf[t / 2]);
+          else
+            mfma16v(s[t % 2], kf, qf[t / 2]);
+          step_hook(t);
         }
-        const int mb = t % MB, ks = t / MB;
-        if (ks == 0)
-          mfma32v_first(s[mb], kf, qf[ks]);
-        else if (t >= N - MB && mb == MB - 1)
-          mfma32v_last(s[mb], kf, qf[ks]);
-        else
-          mfma32v(s[mb], kf, qf[ks]);
-        step_hook(t);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + lane;
+        constexpr int N = MB * KSTEPS;  // step t: key block t % MB, head-dim step t / MB
+        u32x4 kr[kPipeDepth];
+#pragma unroll
+        for (int t = 0; t < kPipeDepth; ++t) kr[t] = kb[((t % MB) * KSTEPS + t / MB) * 64];
+        after_first_reads();
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 kf = as_bf16x8(kr[t % kPipeDepth]);
+          if (t + kPipeDepth < N) {
+            const int u = t + kPipeDepth;
+            kr[t % kPipeDepth] = kb[((u % MB) * KSTEPS + u / MB) * 64];
+          }
+          const int mb = t % MB, ks = t / MB;
+          if (ks == 0)
+            mfma32v_first(s[mb], kf, qf[ks]);
+          else if (t >= N - MB && mb == MB - 1)
+            mfma32v_last(s[mb], kf, qf[ks]);
+          else
+            mfma32v(s[mb], kf, qf[ks]);
+          step_hook(t);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     };
 
     // Causal / window mask of key tile j; only tiles on the diagonal or at
@@ -1093,16 +1156,27 @@ k_prefill4(PrefillArgs a) {
       const int kbase = j * BN;
       return (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
     };
-    auto mask = [&](int j, f32x16 (&s)[MB]) {
+    auto mask = [&](int j, SArr& s) {
       const int kbase = j * BN;
+      if constexpr (R64) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
-          const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
-          s[mb][rr] = vis ? s[mb][rr] : kNegInf;
-        }
+          for (int ii = 0; ii < 4; ++ii) {
+            const int key = kbase + 16 * mb + 4 * grp + ii;
+            const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+            s[mb][ii] = vis ? s[mb][ii] : kNegInf;
+          }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
+            const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+            s[mb][rr] = vis ? s[mb][rr] : kNegInf;
+          }
+      }
     };
 
     // Online softmax of one (masked) tile for this wave's rows.  Each row
@@ -1113,33 +1187,65 @@ k_prefill4(PrefillArgs a) {
     // the pass as outgrown and the work-group repeats the segment from a
     // higher reference (see below).  P^T (bf16) goes to exchange buffer
     // `buf`.  Branch-free, so it shares a scheduling region with the PV MFMAs.
-    auto softmax = [&](f32x16 (&s)[MB], int buf) {
-      float mx = kNegInf;
+    // 64-row tiles: P^T of this lane's 4 + 4 keys goes to half (grp >> 1) of
+    // slot 16 (wave & 1) + j16 + 32 (grp & 1) of row block wave >> 1.
+    auto publish64 = [&](const unsigned (&pk)[4], int buf) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int kv = 0; kv < 2; ++kv)
+        reinterpret_cast<u32x2*>(&sp[buf][wave >> 1][kv][16 * (wave & 1) + j16 + 32 * (grp & 1)])[grp >> 1] =
+            u32x2{pk[2 * kv], pk[2 * kv + 1]};
+    };
+    auto softmax = [&](SArr& s, int buf) {
+      if constexpr (R64) {
+        float mx = kNegInf;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
-      mx = max_lane_pair(mx);
-      m_seen = fmaxf(m_seen, mx);
-      m_i = (m_i == kNegInf) ? mx : m_i;  // nothing accumulated yet: adopt
-      outgrown |= mx > m_i + kMaxGrowth;
-      const float m_use = (m_i == kNegInf) ? 0.f : m_i;
-      float rs = 0.f;
-      unsigned pk[MB * 8];
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+          for (int ii = 0; ii < 4; ++ii) mx = fmaxf(mx, s[mb][ii]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = max_lane_pair(mx);
+        m_seen = fmaxf(m_seen, mx);
+        m_i = (m_i == kNegInf) ? mx : m_i;
+        outgrown |= mx > m_i + kMaxGrowth;
+        const float m_use = (m_i == kNegInf) ? 0.f : m_i;
+        float rs = 0.f;
+        unsigned pk[4];
 #pragma unroll
-        for (int rr = 0; rr < 16; rr += 2) {
-          const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
+        for (int k = 0; k < 4; ++k) {
+          const float p0 = fast_exp2(s[k / 2][2 * (k % 2)] - m_use), p1 = fast_exp2(s[k / 2][2 * (k % 2) + 1] - m_use);
           rs += p0 + p1;
-          pk[mb * 8 + rr / 2] = pack_bf16(p0, p1);
+          pk[k] = pack_bf16(p0, p1);
         }
-      l_i += rs;
-      // P^T slot t of key-step kv is key 16 kv + 4 h + t (t < 4) or
-      // 16 kv + 8 + 4 h + (t - 4): the order the value image stores V in.
+        l_i += rs;
+        publish64(pk, buf);
+      } else {
+        float mx = kNegInf;
 #pragma unroll
-      for (int kv = 0; kv < KV; ++kv)
-        sp[buf][wave][kv][lane] = u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]};
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+        mx = max_lane_pair(mx);
+        m_seen = fmaxf(m_seen, mx);
+        m_i = (m_i == kNegInf) ? mx : m_i;  // nothing accumulated yet: adopt
+        outgrown |= mx > m_i + kMaxGrowth;
+        const float m_use = (m_i == kNegInf) ? 0.f : m_i;
+        float rs = 0.f;
+        unsigned pk[MB * 8];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rr = 0; rr < 16; rr += 2) {
+            const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
+            rs += p0 + p1;
+            pk[mb * 8 + rr / 2] = pack_bf16(p0, p1);
+          }
+        l_i += rs;
+        // P^T slot t of key-step kv is key 16 kv + 4 h + t (t < 4) or
+        // 16 kv + 8 + 4 h + (t - 4): the order the value image stores V in.
+#pragma unroll
+        for (int kv = 0; kv < KV; ++kv)
+          sp[buf][wave][kv][lane] = u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]};
+      }
     };
 
     // O^T += V^T P^T for one key tile over all four row blocks and this
@@ -1175,13 +1281,16 @@ k_prefill4(PrefillArgs a) {
     // the machine scheduler, and an empty asm that takes each stage's result
     // keeps the IR optimisers from sinking the stage to its first use.  The operands of key step 0 arrive in `o0` (loaded during the
     // score chain); those of step kv+1 are read at the start of step kv.
-    auto pv_softmax = [&](const uint16_t* cv, int pbuf, PvOps& o0, f32x16 (&s)[MB], int sbuf) {
+    auto pv_softmax = [&](const uint16_t* cv, int pbuf, PvOps& o0, SArr& s, int sbuf) {
       constexpr int PER_KV = DBW * RB;
       constexpr int NM = KV * PER_KV;
-      constexpr int NPAIR = MB * 8;
+      constexpr int NPAIR = R64 ? 4 : MB * 8;  // exponential pairs per lane
+      // score pair k of this lane (first element's block and register)
+      auto pmb = [](int k) { return R64 ? k / 2 : k / 8; };
+      auto prr = [](int k) { return R64 ? 2 * (k % 2) : 2 * (k % 8); };
       PvOps o1;
       float mx = kNegInf, m_use = 0.f, rs = 0.f;
-      unsigned pk[MB * 8];
+      unsigned pk[NPAIR];
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int kv = t / PER_KV, db = (t / RB) % DBW, rb = t % RB;
@@ -1191,12 +1300,20 @@ k_prefill4(PrefillArgs a) {
         acc[rb][db] = mfma32(as_bf16x8(cur.v[db]), as_bf16x8(cur.p[rb]), acc[rb][db]);
         __builtin_amdgcn_sched_barrier(0);
         if (t == 0) {
+          if constexpr (R64) {
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+              for (int ii = 0; ii < 4; ++ii) mx = fmaxf(mx, s[mb][ii]);
+          } else {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+          }
           asm volatile("" : "+v"(mx));
         } else if (t == 1) {
+          if constexpr (R64) mx = fmaxf(mx, __shfl_xor(mx, 16));
           mx = max_lane_pair(mx);
           m_seen = fmaxf(m_seen, mx);
           m_i = (m_i == kNegInf) ? mx : m_i;  // nothing accumulated yet: adopt
@@ -1204,7 +1321,7 @@ k_prefill4(PrefillArgs a) {
           m_use = (m_i == kNegInf) ? 0.f : m_i;
           asm volatile("" : "+v"(m_use));
         } else if (t - 2 < NPAIR) {
-          const int k = t - 2, mb = k / 8, rr = 2 * (k % 8);
+          const int k = t - 2, mb = pmb(k), rr = prr(k);
           const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
           rs += p0 + p1;
           pk[k] = pack_bf16(p0, p1);
@@ -1214,23 +1331,26 @@ k_prefill4(PrefillArgs a) {
       }
 #pragma unroll
       for (int k = NM - 2; k < NPAIR; ++k) {  // pairs left over when there are few MFMAs
-        const int mb = k / 8, rr = 2 * (k % 8);
+        const int mb = pmb(k), rr = prr(k);
         const float p0 = fast_exp2(s[mb][rr] - m_use), p1 = fast_exp2(s[mb][rr + 1] - m_use);
         rs += p0 + p1;
         pk[k] = pack_bf16(p0, p1);
       }
       l_i += rs;
+      if constexpr (R64) {
+        publish64(pk, sbuf);
+      } else {
 #pragma unroll
-      for (int kv = 0; kv < KV; ++kv)
-        sp[sbuf][wave][kv][lane] = u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]};
+        for (int kv = 0; kv < KV; ++kv)
+          sp[sbuf][wave][kv][lane] = u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]};
+      }
     };
 
     // One pass over key tiles jb..je.  Returns false when a row of the
     // work-group outgrew its reference maximum (the accumulated values are
     // then unusable); the caller repeats the pass from the largest scores
     // seen.  The pass always runs to its end, so the loop has a single exit.
-    const int nt = je - jb + 1;
-    auto pass = [&]() __attribute__((always_inline)) -> bool {
+    auto pass = [&](bool first) __attribute__((always_inline)) -> bool {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -1238,13 +1358,15 @@ k_prefill4(PrefillArgs a) {
       m_i = m_init;
       l_i = 0.f;
       outgrown = false;
-      issue_k(jb, sk[0]);
-      wait_vm<0>();
+      if (!first) issue_head();
+      // key tile jb has landed (copies complete in issue order)
+      if (1 < nt)
+        wait_vm<2 * LPT>();
+      else
+        wait_vm<LPT>();
       lds_barrier();
-      if (1 < nt) issue_k(jb + 1, sk[1]);
-      issue_v(jb, sv[0]);
       {
-        f32x16 s[MB];
+        SArr s;
         scores(sk[0], s, [] {}, [](int) {});
         if (needs_mask(jb)) mask(jb, s);
         softmax(s, 0);
@@ -1253,7 +1375,7 @@ k_prefill4(PrefillArgs a) {
         wait_vm<0>();   // key tile i and value tile i-1 (issued one iteration ago) have landed
         lds_barrier();  // ... for every wave; P(i-1) is published; buffers (i+1)&1 are free
         const int pb = (i - 1) & 1;
-        f32x16 s[MB];
+        SArr s;
         PvOps o0;
         // The copies of key tile i+1 and value tile i are spread over the
         // score chain, one per two MFMAs: issued back to back they would hold
@@ -1290,9 +1412,11 @@ k_prefill4(PrefillArgs a) {
       lds_barrier();  // the words are read before anybody refills the buffer
       return !any;
     };
-    while (!pass()) {
+    bool first = true;
+    while (!pass(first)) {
       // Nothing is in flight and every wave has passed the last barrier.
       m_init = m_seen;
+      first = false;
     }
 
     const size_t slot_f4 = (size_t)ACC_F4 + 4 * 64 / 2;
@@ -1307,7 +1431,7 @@ k_prefill4(PrefillArgs a) {
       const int p = rr / a.g, hd = kvh * a.g + rr % a.g;
       return a.out + (((size_t)b * a.S + p) * a.Hq + hd) * D + 32 * wave * DBW;
     };
-    if (jb != jlo_t || je != jhi_t) {
+    if (!R64 && (jb != jlo_t || je != jhi_t)) {  // (64-row tiles are never cut into pieces)
       // Partial: store (O, m, l), then count this piece in (see k_prefill).
       auto slot_rsrc = [&](int pc) {
         f32x4* p = reinterpret_cast<f32x4*>(a.part) + (((size_t)bh * a.npair + pair) * a.kpieces + pc) * 2 * slot_f4 +
@@ -1495,11 +1619,17 @@ k_prefill4(PrefillArgs a) {
     // Whole tile here: the row blocks' denominators meet in LDS (the key
     // buffers are idle once the last PV has started).
     float* sl = reinterpret_cast<float*>(&sk[0][0]);
-    sl[wave * 64 + lane] = l_i + __shfl_xor(l_i, 32);
+    if constexpr (R64) {
+      float lt = l_i + __shfl_xor(l_i, 16);
+      lt += __shfl_xor(lt, 32);
+      if (grp == 0) sl[wave * 16 + j16] = lt;
+    } else {
+      sl[wave * 64 + lane] = l_i + __shfl_xor(l_i, 32);
+    }
     lds_barrier();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float lt = sl[rb * 64 + lane];
+      const float lt = R64 ? sl[32 * rb + n] : sl[rb * 64 + lane];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       float* orow = out_row(rb);
       if (orow) {
@@ -1896,9 +2026,9 @@ void fill_rope_rev(RopeRev* r, int head_dim, double theta) {
 }
 
 // Key tiles a 128-row query tile visits (same rule as the kernel).
-static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int& jlo, int& jhi) {
-  const int rows_total = S * g, r0 = qt * kPrefillRows;
-  const int pmin = r0 / g, pmax = std::min(r0 + kPrefillRows - 1, rows_total - 1) / g;
+static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int rows, int& jlo, int& jhi) {
+  const int rows_total = S * g, r0 = qt * rows;
+  const int pmin = r0 / g, pmax = std::min(r0 + rows - 1, rows_total - 1) / g;
   jlo = (W > 0 ? std::max(0, pmin - W + 1) : 0) / BN;
   jhi = pmax / BN;
 }
@@ -1907,6 +2037,8 @@ static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int& jlo, int
 // which evens out causal tiles, or a single query tile, which suits
 // windowed layers whose tiles all visit about the same number of key tiles;
 // each unit's key work is cut into kpieces ranges, one per work-group.
+// Head size 256 may also run 64-row query tiles (twice the work-groups, no
+// pieces), which fills the GPU when 128-row tiles are too few.
 // The choice minimises an estimate of the slowest work-group's time: key
 // tiles times the per-tile cost, plus a fixed cost per query-tile segment
 // (query load and rotation, first tile copy, output) and, when a tile is
@@ -1915,9 +2047,19 @@ static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int& jlo, int
 struct PrefillCosts {
   double tile, segment, split;
 };
-static PrefillCosts prefill_costs(int D) {
+static PrefillCosts prefill_costs(int D, int rows) {
   if (D == 512) return {4700.0, 12000.0, 40000.0};
+  if (rows == 64) return {1400.0, 12000.0, 0.0};
   return {2400.0, 15000.0, 30000.0};
+}
+
+// G4_PREFILL_ROWS=128 or 64 pins the query-tile height of head size 256
+// (tests use it to reach both kernels at small sizes); unset = cost model.
+static int prefill_rows_override() {
+  const char* e = std::getenv("G4_PREFILL_ROWS");
+  if (!e) return 0;
+  const int v = std::atoi(e);
+  return (v == 64 || v == 128) ? v : 0;
 }
 
 PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
@@ -1925,34 +2067,42 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   p.BN = prefill_key_tile(D);
   p.ntiles = ceil_div(S, p.BN);
   p.g = Hq / Hkv;
-  p.nqt = ceil_div(S * p.g, kPrefillRows);
-  const PrefillCosts c = prefill_costs(D);
+  const int forced = D == 256 ? prefill_rows_override() : 0;
   double best = 0.0;
-  for (int paired = 1; paired >= 0; --paired) {
-    const int nunits = paired ? (p.nqt + 1) / 2 : p.nqt;
-    // largest key work of a unit bounds the useful number of pieces
-    int umax = 1;
-    for (int i = 0; i < nunits; ++i) {
-      int a0, a1, b0 = 0, b1 = -1;
-      if (paired) {
-        prefill_tile_keys(p.nqt - 1 - i, S, p.g, W, p.BN, a0, a1);
-        if (i < p.nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, b0, b1);
-      } else {
-        prefill_tile_keys(i, S, p.g, W, p.BN, a0, a1);
+  for (int rows : {128, 64}) {
+    if (rows == 64 && D != 256) continue;
+    if (forced && rows != forced) continue;
+    const int nqt = ceil_div(S * p.g, rows);
+    const PrefillCosts c = prefill_costs(D, rows);
+    for (int paired = 1; paired >= 0; --paired) {
+      const int nunits = paired ? (nqt + 1) / 2 : nqt;
+      // largest key work of a unit bounds the useful number of pieces
+      int umax = 1;
+      for (int i = 0; i < nunits; ++i) {
+        int a0, a1, b0 = 0, b1 = -1;
+        if (paired) {
+          prefill_tile_keys(nqt - 1 - i, S, p.g, W, p.BN, rows, a0, a1);
+          if (i < nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, rows, b0, b1);
+        } else {
+          prefill_tile_keys(i, S, p.g, W, p.BN, rows, a0, a1);
+        }
+        umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
       }
-      umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
-    }
-    const long groups = (long)B * Hkv * nunits;
-    const int kmax = (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
-    for (int k = 1; k <= kmax; ++k) {
-      const double rounds = std::ceil((double)groups * k / kPrefillSlots);
-      const double segs = paired ? (k <= 2 ? 2.0 : 1.5) : 1.0;
-      const double t = rounds * (std::ceil((double)umax / k) * c.tile + segs * c.segment + (k > 1 ? c.split : 0.0));
-      if (best == 0.0 || t < best) {
-        best = t;
-        p.paired = paired;
-        p.npair = nunits;
-        p.kpieces = k;
+      const long groups = (long)B * Hkv * nunits;
+      const int kmax =
+          rows == 64 ? 1 : (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
+      for (int k = 1; k <= kmax; ++k) {
+        const double rounds = std::ceil((double)groups * k / kPrefillSlots);
+        const double segs = paired ? (k <= 2 ? 2.0 : 1.5) : 1.0;
+        const double t = rounds * (std::ceil((double)umax / k) * c.tile + segs * c.segment + (k > 1 ? c.split : 0.0));
+        if (best == 0.0 || t < best) {
+          best = t;
+          p.rows = rows;
+          p.nqt = nqt;
+          p.paired = paired;
+          p.npair = nunits;
+          p.kpieces = k;
+        }
       }
     }
   }
@@ -2010,7 +2160,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
     hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
-    hipLaunchKernelGGL((k_prefill4<256, 32>), grid_a, dim3(256), 0, stream, a);
+    if (pl.rows == 64)
+      hipLaunchKernelGGL((k_prefill4<256, 32, 64>), grid_a, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_prefill4<256, 32, 128>), grid_a, dim3(256), 0, stream, a);
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   return hipGetLastError();

@@ -110,48 +110,61 @@ def test_kv_bytes_and_sharing(lib):
     assert total_k + total_v == 12 * 2048 * 256 * 2 + 3 * 2 * (2 * 2048 * 512 * 2) == 37748736
 
 
-def _prefill_ws_model(B, S, Hq, Hkv, D, W):
+def _prefill_ws_model(B, S, Hq, Hkv, D, W, rows_forced=None):
     """Workspace layout of a prefill call: key and value operand images,
     arrival counters, partial-result slots of the query tiles split across
     work-groups.  The work split is chosen by the same cost model as the
-    library (per-tile, per-segment and per-split cycle costs)."""
+    library (per-tile, per-segment and per-split cycle costs; head size 256
+    also considers 64-row query tiles, which are never split).  Returns
+    (bytes, pieces, rows)."""
     import math
     BN = 32
     ntiles = -(-S // BN)
     g = Hq // Hkv
-    nqt = -(-(S * g) // 128)
-
-    def keys(qt):
-        r0 = qt * 128
-        pmin, pmax = r0 // g, min(r0 + 127, S * g - 1) // g
-        return (max(0, pmin - W + 1) if W > 0 else 0) // BN, pmax // BN
-
-    tile, segment, split = (4700.0, 12000.0, 40000.0) if D == 512 else (2400.0, 15000.0, 30000.0)
     best = None
-    for paired in (1, 0):
-        nunits = (nqt + 1) // 2 if paired else nqt
-        umax = 1
-        for i in range(nunits):
-            if paired:
-                a0, a1 = keys(nqt - 1 - i)
-                b0, b1 = keys(i) if i < nqt - 1 - i else (0, -1)
-            else:
-                (a0, a1), (b0, b1) = keys(i), (0, -1)
-            umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
-        groups = B * Hkv * nunits
-        for k in range(1, max(1, min(256 // groups, umax, 64)) + 1):
-            rounds = math.ceil(groups * k / 256)
-            segs = (2.0 if k <= 2 else 1.5) if paired else 1.0
-            t = rounds * (math.ceil(umax / k) * tile + segs * segment + (split if k > 1 else 0.0))
-            if best is None or t < best[0]:
-                best = (t, groups, k)
-    _, groups, k = best
+    for rows in (128, 64):
+        if rows == 64 and D != 256:
+            continue
+        if rows_forced and rows != rows_forced:
+            continue
+        nqt = -(-(S * g) // rows)
+
+        def keys(qt):
+            r0 = qt * rows
+            pmin, pmax = r0 // g, min(r0 + rows - 1, S * g - 1) // g
+            return (max(0, pmin - W + 1) if W > 0 else 0) // BN, pmax // BN
+
+        if D == 512:
+            tile, segment, split = 4700.0, 12000.0, 40000.0
+        elif rows == 64:
+            tile, segment, split = 1400.0, 12000.0, 0.0
+        else:
+            tile, segment, split = 2400.0, 15000.0, 30000.0
+        for paired in (1, 0):
+            nunits = (nqt + 1) // 2 if paired else nqt
+            umax = 1
+            for i in range(nunits):
+                if paired:
+                    a0, a1 = keys(nqt - 1 - i)
+                    b0, b1 = keys(i) if i < nqt - 1 - i else (0, -1)
+                else:
+                    (a0, a1), (b0, b1) = keys(i), (0, -1)
+                umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
+            groups = B * Hkv * nunits
+            kmax = 1 if rows == 64 else max(1, min(256 // groups, umax, 64))
+            for k in range(1, kmax + 1):
+                rounds = math.ceil(groups * k / 256)
+                segs = (2.0 if k <= 2 else 1.5) if paired else 1.0
+                t = rounds * (math.ceil(umax / k) * tile + segs * segment + (split if k > 1 else 0.0))
+                if best is None or t < best[0]:
+                    best = (t, groups, k, rows, nqt)
+    _, groups, k, rows, nqt = best
     img = -(-(B * Hkv * ntiles * BN * D * 2) // 256) * 256
     cnt = 2 * img
     part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256
     nw = 8 if D == 512 else 4  # waves per work-group
     slot = 32 * D * 16 + nw * 64 * 2 * 4
-    return part + (groups * k * 2 * slot if k > 1 else 0), k
+    return part + (groups * k * 2 * slot if k > 1 else 0), k, rows
 
 
 def test_workspace_sizes(lib):
@@ -159,10 +172,12 @@ def test_workspace_sizes(lib):
     for layer in (0, 4):
         d = stack[layer]
         for S in (1, 100, 2048, 4096):
-            want, _ = _prefill_ws_model(1, S, d["num_q_heads"], d["num_kv_heads"], d["head_dim"], d["window"])
+            want = _prefill_ws_model(1, S, d["num_q_heads"], d["num_kv_heads"], d["head_dim"], d["window"])[0]
             assert L.prefill_workspace_bytes(stack, layer, 1, S) == want
     # the 4096-token full layer is cut into two pieces per pair of query tiles
     assert _prefill_ws_model(1, 4096, 8, 2, 512, 0)[1] == 2
+    # the stack's sliding layers (128 tiles of 128 rows) run 64-row tiles
+    assert _prefill_ws_model(1, 2048, 8, 1, 256, 512)[2] == 64
     assert L.prefill_workspace_bytes(stack, 0, 1, 2048) >= 1 * 1 * 2048 * 256 * 2
     w = L.decode_workspace_bytes(stack, 4, 64, 8192)
     assert w > 0 and w % 4 == 0

@@ -85,6 +85,24 @@ def test_prefill_shapes(B, S, Hq, Hkv, D, W, alias, Lmax):
                   alias, Lmax)
 
 
+@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("B,S,Hq,Hkv,W,alias,Lmax", [
+    (2, 333, 8, 1, 48, True, 333),      # sliding K=V, batch 2, ragged
+    (1, 130, 2, 2, 16, False, 130),     # no GQA sharing, separate V
+    (1, 1, 4, 1, 32, True, 1),          # single token
+    (3, 257, 16, 2, 100, True, 300),    # GQA group of 8, three sequences, poisoned tail
+    (1, 200, 8, 2, 0, False, 256),      # causal, ragged, poisoned tail
+    (1, 1024, 8, 1, 0, False, 1024),    # causal: 128-row tiles cut into pieces
+    (1, 2048, 4, 1, 0, False, 2048),    # causal: pairs of 128-row tiles in up to 8 pieces
+    (1, 1000, 8, 1, 512, True, 1000),   # the stack's sliding-layer configuration, shorter
+])
+def test_prefill_head256_tile_heights(monkeypatch, rows, B, S, Hq, Hkv, W, alias, Lmax):
+    """Head size 256 runs 128-row or 64-row query tiles; both against the oracle."""
+    monkeypatch.setenv("G4_PREFILL_ROWS", str(rows))
+    _prefill_case("prefill rows%d B%d S%d Hq%d Hkv%d W%d alias%d" % (rows, B, S, Hq, Hkv, W, alias), B, S, Hq, Hkv,
+                  256, W, alias, Lmax)
+
+
 def test_prefill_window_one_is_identity_on_raw_keys():
     got = _prefill_case("window1", 1, 40, 4, 1, 256, 1, True)
     k = inputs.normal_bf16([100, 40, 1], (1, 1, 40, 256))
