@@ -207,6 +207,52 @@ def bench_decode(steps, warmup):
     }
 
 
+def bench_decode_long(steps, warmup):
+    """Long-context decode: B=4, per-sequence KV lengths uniform in [1024, 131072]
+    (seeded), full layer (D=512, Hq=16, Hkv=2) and sliding layer (D=256, Hq=16,
+    Hkv=2, window 1024, K=V); caches flushed from L2/MALL before every call."""
+    import torch
+    from hybrid_sliding_global_amd import Stack, inputs
+    from hybrid_sliding_global_amd import workloads as wl
+    w = wl.workloads()[5]
+    B, Lmax = w.batch, w.max_len
+    kv = inputs.kv_lengths_uniform([5, 0, inputs.TENSOR_LEN], B, w.kv_len_range[0], w.kv_len_range[1])
+    kl = torch.from_numpy(kv).to("cuda:0")
+    max_kv = int(kv.max())
+    flush_buf = torch.empty(1 << 29, dtype=torch.uint8, device="cuda:0")  # 512 MiB > the 256 MB MALL
+
+    def flush():
+        flush_buf.fill_(1)
+
+    res = {}
+    for li, d in enumerate(w.layers):
+        D, Hq, Hkv = d["head_dim"], d["num_q_heads"], d["num_kv_heads"]
+        q = dev(inputs.normal_bf16([5, li, inputs.TENSOR_Q], (B, Hq, D)))
+        k = dev(inputs.normal_bf16([5, li, inputs.TENSOR_K], (B, Hkv, Lmax, D)))
+        v = None if d["kv_alias"] else dev(inputs.normal_bf16([5, li, inputs.TENSOR_V], (B, Hkv, Lmax, D)))
+        st = Stack([d])
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(st.decode_workspace_bytes(0, B, max_kv), dtype=torch.uint8, device="cuda:0")
+
+        def step():
+            st.decode(0, q, [k], [v], kl, max_kv, out=out, workspace=ws)
+
+        call_ms, kern_ms = time_calls(step, steps, warmup, flush=flush)
+        nbytes = wl.decode_bytes(kv, Hq, Hkv, D, d["window"], bool(d["kv_alias"]))
+        name = "full" if d["kind"] == wl.FULL else "sliding"
+        res[name] = {"bytes": nbytes, "ms_per_call": call_ms, "kernel_ms": kern_ms,
+                     "GB/s": nbytes / (call_ms * 1e-3) / 1e9, "kernel_GB/s": nbytes / (kern_ms * 1e-3) / 1e9}
+        del q, k, v
+    full = res["full"]
+    return {
+        "workload": "decode_b4_long (KV lengths %s; full hd512 Hq16/Hkv2 + sliding hd256 Hq16/Hkv2 W1024 K=V)"
+                    % kv.tolist(),
+        "unit": "GB/s", "layers": res,
+        "roofline": {"bound": "hbm", "achieved": full["kernel_GB/s"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": full["kernel_GB/s"] / PEAK_HBM_GBS},
+    }
+
+
 def bench_stack(steps):
     """35-layer prefill stack (B=1, S=2048; 28 sliding hd256 W512 K=V + 7 full hd512, 15 owned caches):
     one pass = every layer's prefill call, in order, on one stream."""
@@ -276,6 +322,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-long-decode", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -323,6 +370,12 @@ def main():
         line["decode"] = bench_decode(max(5, args.steps // 2), 2)
         log("decode: %.1f GB/s (full-layer kernel %.1f GB/s)" %
             (line["decode"]["value"], line["decode"]["layers"]["full"]["kernel_GB/s"]))
+    if not args.no_decode and not args.no_long_decode:
+        log("decode: B=4, long contexts")
+        line["long_decode"] = bench_decode_long(max(5, args.steps // 2), 2)
+        log("decode long: full-layer kernel %.1f GB/s, sliding-layer kernel %.1f GB/s" %
+            (line["long_decode"]["layers"]["full"]["kernel_GB/s"],
+             line["long_decode"]["layers"]["sliding"]["kernel_GB/s"]))
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on sampled rows")
         line["cpu_baseline"] = cpu_baseline(pre)

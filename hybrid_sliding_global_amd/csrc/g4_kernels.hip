@@ -1958,46 +1958,62 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   }
 }
 
-// Log-sum-exp merge of the chunk partials of one (batch, head).  256
-// threads: thread t owns head-dim quad t % (D/4) and every (256/(D/4))-th
-// chunk starting at t / (D/4); the chunk groups are summed through LDS.
+// Log-sum-exp merge of the chunk partials of one (batch, head) and one
+// 64-wide head-dim slice.  256 threads: thread t owns quad t % 16 of the
+// slice and every 16th chunk starting at t / 16; the chunk groups are summed
+// through LDS in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_lse, float* __restrict__ out,
                                                         int nchunks) {
-  constexpr int NQ = D / 4;        // head-dim quads
+  // Work-group (query head bh, 64-wide head-dim slice blockIdx.y): 16 quads
+  // of the slice, 16 groups of chunks, so that even a few heads with long
+  // contexts (many chunks) spread over enough work-groups.
+  constexpr int NQ = 16;           // head-dim quads per work-group
   constexpr int NGRP = 256 / NQ;   // chunk groups
+  static_assert(D % (4 * NQ) == 0, "head dim splits into 64-wide slices");
   __shared__ f32x4 snum[NGRP][NQ];
   __shared__ float sden[NGRP][NQ];
+  __shared__ float smax[4];
   const int bh = blockIdx.x;
   const int qd = threadIdx.x % NQ, grp = threadIdx.x / NQ;
   const float* lse = part_lse + (size_t)bh * nchunks;
+  // Largest chunk log-sum-exp: a strided share per thread (one load each for
+  // up to 256 chunks), then the wave and work-group maxima.
   float M = kNegInf;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, lse[c]);
-  const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (size_t)bh * nchunks * D) + qd;
+  for (int c = threadIdx.x; c < nchunks; c += 256) M = fmaxf(M, lse[c]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (size_t)bh * nchunks * D) + blockIdx.y * NQ + qd;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
+  // chunks grp, grp + NGRP, ...: four loads in flight per round trip (empty
+  // chunks, lse = -inf, never wrote their partial: their loads are discarded)
+  constexpr int U = 4;
   int c = grp;
-  for (; c + 3 * NGRP < nchunks; c += 4 * NGRP) {
-    f32x4 o[4];
-    float w[4];
+  for (; c + (U - 1) * NGRP < nchunks; c += U * NGRP) {
+    f32x4 o[U];
+    float e[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float e = lse[c + u * NGRP];
-      w[u] = e == kNegInf ? 0.f : fast_exp2(e - M);
-      o[u] = e == kNegInf ? f32x4{0.f, 0.f, 0.f, 0.f} : po[(size_t)(c + u * NGRP) * NQ];
+    for (int u = 0; u < U; ++u) {
+      e[u] = lse[c + u * NGRP];
+      o[u] = po[(size_t)(c + u * NGRP) * (D / 4)];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      num += w[u] * o[u];
-      den += w[u];
+    for (int u = 0; u < U; ++u) {
+      const float w = e[u] == kNegInf ? 0.f : fast_exp2(e[u] - M);
+      num += w * (e[u] == kNegInf ? f32x4{0.f, 0.f, 0.f, 0.f} : o[u]);
+      den += w;
     }
   }
   for (; c < nchunks; c += NGRP) {
     const float e = lse[c];
     if (e == kNegInf) continue;
     const float w = fast_exp2(e - M);
-    num += w * po[(size_t)c * NQ];
+    num += w * po[(size_t)c * (D / 4)];
     den += w;
   }
   snum[grp][qd] = num;
@@ -2009,7 +2025,7 @@ __global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict_
       num += snum[g2][qd];
       den += sden[g2][qd];
     }
-    reinterpret_cast<f32x4*>(out + (size_t)bh * D)[qd] = num * (1.f / den);
+    reinterpret_cast<f32x4*>(out + (size_t)bh * D)[blockIdx.y * NQ + qd] = num * (1.f / den);
   }
 }
 
@@ -2222,11 +2238,11 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   if (p.D == 512)
-    hipLaunchKernelGGL((k_decode_combine<512>), dim3(p.B * p.Hq), dim3(256), 0, stream, a.part_o, a.part_lse, p.out,
-                       a.nchunks);
+    hipLaunchKernelGGL((k_decode_combine<512>), dim3(p.B * p.Hq, 512 / 64), dim3(256), 0, stream, a.part_o,
+                       a.part_lse, p.out, a.nchunks);
   else
-    hipLaunchKernelGGL((k_decode_combine<256>), dim3(p.B * p.Hq), dim3(256), 0, stream, a.part_o, a.part_lse, p.out,
-                       a.nchunks);
+    hipLaunchKernelGGL((k_decode_combine<256>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a.part_o,
+                       a.part_lse, p.out, a.nchunks);
   return hipGetLastError();
 }
 
