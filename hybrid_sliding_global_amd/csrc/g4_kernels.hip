@@ -260,13 +260,6 @@ __device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsi
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
                : "memory", "m0");
 }
-// The same copy from a 64-bit per-lane address (VGPR pair), for kernels
-// whose scalar registers are too scarce to hold a tile base.
-__device__ __forceinline__ void dma_block_v(const void* gbase, unsigned voff, unsigned lds) {
-  const uint64_t addr = reinterpret_cast<uint64_t>(gbase) + voff;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds)
-               : "memory", "m0");
-}
 #pragma clang diagnostic pop
 
 // Operand images of one key tile, written once per prefill call so that the
@@ -912,6 +905,7 @@ template <int D, int BN, int ROWS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 k_prefill4(PrefillArgs a) {
   static_assert(ROWS == 128 || ROWS == 64, "query tile of 128 or 64 rows");
+  static_assert(D == 256, "one wave per SIMD holds the queries and output block of head size 256 only");
   constexpr bool R64 = ROWS == 64;   // 16 score rows per wave (16x16x32 MFMAs), no split pieces
   constexpr int KSTEPS = D / 16;     // 32x32x16 steps over the head dim
   constexpr int MB = BN / 32;        // 32-key blocks per tile
@@ -970,13 +964,7 @@ k_prefill4(PrefillArgs a) {
   const uint16_t* vimg = a.vimg + slice_off;
   const unsigned voff = (unsigned)(wave * 1024 + lane * 16);
 
-  // Head size 512 leaves too few scalar registers for the tile bases.
-  auto copy_block = [&](const void* g, unsigned vo, unsigned l) {
-    if constexpr (D == 512)
-      dma_block_v(g, vo, l);
-    else
-      dma_block(g, vo, l);
-  };
+  auto copy_block = [&](const void* g, unsigned vo, unsigned l) { dma_block(g, vo, l); };
   auto issue_k = [&](int j, uint16_t* dk) {
     const char* kt = reinterpret_cast<const char*>(kimg + (size_t)j * (BN * D));
     const unsigned lk = lds_addr(dk) + wave * 1024;
