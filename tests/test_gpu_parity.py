@@ -79,6 +79,7 @@ def test_workload1_sliding_prefill_full_compare():
     (1, 1024, 8, 1, 256, 0, False, 1024),  # single query tiles in up to 4 pieces
     (1, 2048, 4, 1, 256, 0, False, 2048),  # pairs of query tiles in up to 8 pieces
     (1, 640, 8, 2, 512, 0, False, 640),    # head size 512, pairs cut into 11 pieces
+    (1, 37, 160, 1, 512, 0, False, 40),    # GQA group of 160: a 128-row tile spans parts of two positions
 ])
 def test_prefill_shapes(B, S, Hq, Hkv, D, W, alias, Lmax):
     _prefill_case("prefill B%d S%d Hq%d Hkv%d D%d W%d alias%d" % (B, S, Hq, Hkv, D, W, alias), B, S, Hq, Hkv, D, W,
@@ -95,6 +96,7 @@ def test_prefill_shapes(B, S, Hq, Hkv, D, W, alias, Lmax):
     (1, 1024, 8, 1, 0, False, 1024),    # causal: 128-row tiles cut into pieces
     (1, 2048, 4, 1, 0, False, 2048),    # causal: pairs of 128-row tiles in up to 8 pieces
     (1, 1000, 8, 1, 512, True, 1000),   # the stack's sliding-layer configuration, shorter
+    (1, 45, 96, 1, 16, True, 45),       # GQA group of 96: one position per 64-row tile, less than one per row block
 ])
 def test_prefill_head256_tile_heights(monkeypatch, rows, B, S, Hq, Hkv, W, alias, Lmax):
     """Head size 256 runs 128-row or 64-row query tiles; both against the oracle."""
