@@ -157,7 +157,7 @@ G4_EXPORT int gemma4_decode_workspace_bytes(const g4_layer_desc* layers, int32_t
   if (batch < 1 || max_kv_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, max_kv_len %d", batch, max_kv_len);
   const g4_layer_desc& d = layers[layer];
   const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, d.window, max_kv_len);
-  *bytes = g4::decode_workspace(batch, d.num_q_heads, d.head_dim, plan);
+  *bytes = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, plan);
   return ok();
 }
 
@@ -221,7 +221,7 @@ G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, 
   if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
   const int W = d.kind == G4_SLIDING ? d.window : 0;
   const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, W, max_kv_len);
-  const size_t need = g4::decode_workspace(batch, d.num_q_heads, d.head_dim, plan);
+  const size_t need = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, plan);
   if (!workspace || workspace_bytes < need)
     return fail(G4_ERR_WORKSPACE, "decode workspace %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
   g4::DecodeLaunch p;

@@ -62,13 +62,13 @@ struct ProfileEvents {
 size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const ProfileEvents& ev);
 
-// Decode split-K planning: keys per work-group and number of chunks.
+// Decode split: the visible keys of all (batch, kv-head) streams are cut
+// into equal pieces on the device (from kv_len), one per work-group.
 struct DecodePlan {
-  int chunk;    // keys per work-group (multiple of 32)
-  int nchunks;  // chunks per (batch, kv-head) stream
+  int npieces;  // work-groups (pieces of at least 64 keys; fewer when the keys are few)
 };
 DecodePlan plan_decode(int B, int Hkv, int W, int max_kv_len);
-size_t decode_workspace(int B, int Hq, int D, const DecodePlan& plan);
+size_t decode_workspace(int B, int Hq, int Hkv, int D, const DecodePlan& plan);
 
 struct DecodeLaunch {
   const void* q;        // bf16 [B, Hq, D]

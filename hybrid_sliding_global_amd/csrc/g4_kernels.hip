@@ -59,6 +59,7 @@ constexpr float kMaxGrowth = 64.f;     // log2 units: largest P = 2^(s - referen
 #ifndef G4_PIPE_DEPTH
 #define G4_PIPE_DEPTH 4
 #endif
+constexpr int kDecodePieces = 512;   // decode work-groups: two per CU of an MI355X
 constexpr int kDecodeStages = 4;      // 16-row key/value stages in the decode LDS ring (2 when K and V
                                       // are both staged at head size 512, so two work-groups share a CU)
 
@@ -1649,9 +1650,10 @@ struct DecodeArgs {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* kv_len;
-  float* part_o;    // [B, Hq, nchunks, D]
-  float* part_lse;  // [B, Hq, nchunks], log2 units
-  int B, Hq, Hkv, g, Lmax, W, nchunks, chunk;
+  float* part_o;    // [slots][g][D]: slot = stream + piece (see k_decode)
+  float* part_lse;  // [slots][g], log2 units
+  int B, Hq, Hkv, g, Lmax, W;
+  int npieces;      // work-groups of the split (pieces of the total key work)
   float qscale;
   RopeRev rope;
 };
@@ -1712,6 +1714,72 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// Visible key count of batch entry b's streams (all its kv heads).
+__device__ __forceinline__ long long decode_batch_keys(const DecodeArgs& a, int b) {
+  const int L = min(max(a.kv_len[b], 1), a.Lmax);
+  const int lo = a.W > 0 ? max(0, L - a.W) : 0;
+  return (long long)a.Hkv * (L - lo);
+}
+
+// Sum over the work-group (256 threads) of one value per thread.
+__device__ __forceinline__ long long block_sum_ll(long long x, long long* red4) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const long long t = red4[0] + red4[1] + red4[2] + red4[3];
+  __syncthreads();  // red4 is read before anybody reuses it
+  return t;
+}
+
+// The split of the decode work: T visible keys over all streams, np pieces
+// (at most a.npieces, at least 64 keys each); for work-group blockIdx.x <
+// np, the batch entry whose streams hold its first key and where they start.
+__device__ void decode_split(const DecodeArgs& a, long long& T, int& np, int& b_lo, long long& base_lo) {
+  __shared__ long long s_red[4];
+  __shared__ long long s_carry, s_base;
+  __shared__ int s_blo;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long t = 0;
+  for (int b = tid; b < a.B; b += 256) t += decode_batch_keys(a, b);
+  T = block_sum_ll(t, s_red);
+  np = (int)min((long long)a.npieces, max(1LL, T / 64));
+  b_lo = 0;
+  base_lo = 0;
+  if ((int)blockIdx.x >= np) return;  // (the whole work-group)
+  const long long r0 = (long long)blockIdx.x * T / np;
+  if (tid == 0) {
+    s_carry = 0;
+    s_blo = 0;  // (exactly one batch entry's range holds r0 and overwrites these)
+    s_base = 0;
+  }
+  __syncthreads();
+  for (int b0 = 0; b0 < a.B; b0 += 256) {
+    const int b = b0 + tid;
+    const long long sz = b < a.B ? decode_batch_keys(a, b) : 0;
+    long long x = sz;  // inclusive scan over the work-group
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_red[wave] = x;
+    __syncthreads();
+    long long pre = s_carry;
+    for (int w = 0; w < wave; ++w) pre += s_red[w];
+    const long long incl = pre + x, excl = incl - sz;
+    if (b < a.B && excl <= r0 && r0 < incl) {
+      s_blo = b;
+      s_base = excl;
+    }
+    __syncthreads();
+    if (tid == 255) s_carry = incl;
+    __syncthreads();
+  }
+  b_lo = s_blo;
+  base_lo = s_base;
+}
+
 // Split-K decode.  Scores need <R_P q, R_j k> (P = kv_len - 1, j = key
 // position); RoPE rotations are orthogonal and commute, so this equals
 // <R_{P - j0} q, R_{j - j0} k> for any j0.  With j0 = the first key of the
@@ -1740,22 +1808,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, G = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = blockIdx.x % a.nchunks;
-  const int bh = blockIdx.x / a.nchunks;
-  const int kvh = bh % a.Hkv, b = bh / a.Hkv;
-  const int L = min(max(a.kv_len[b], 1), a.Lmax);
-  const int lo = a.W > 0 ? max(0, L - a.W) : 0;
-  const int k_start = lo + c * a.chunk;
-  const int k_end = min(L, k_start + a.chunk);
   const bool qvalid = n < a.g;
+
+  // The visible keys of all (batch, kv-head) streams, laid end to end
+  // (batch-major, kv heads of a batch entry adjacent, each stream its window
+  // [lo_b, L_b)), are cut into np equal pieces, one per work-group; a
+  // piece's part of each stream it overlaps is one segment, whose partial
+  // goes to slot (stream + piece) -- unique, as streams and pieces are both
+  // ordered.  k_decode_combine finds the same pieces from kv_len.
+  long long T;
+  int np, b_lo;
+  long long base_lo;
+  decode_split(a, T, np, b_lo, base_lo);
+  const int piece = blockIdx.x;
+  if (piece >= np) return;
+  const long long r0 = (long long)piece * T / np, r1 = (long long)(piece + 1) * T / np;
+
+  auto segment = [&](int b, int kvh, int k_start, int k_end, int slot) __attribute__((always_inline)) {
+  const int L = min(max(a.kv_len[b], 1), a.Lmax);
   const int head = kvh * a.g + (qvalid ? n : 0);
-  const size_t part = ((size_t)b * a.Hq + head) * a.nchunks + c;
-
-  if (k_start >= k_end) {
-    if (wave == 0 && G == 0 && qvalid) a.part_lse[part] = kNegInf;
-    return;
-  }
-
+  const size_t part = (size_t)slot * a.g + (qvalid ? n : 0);
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   auto issue = [&](int step, int stg) {
     int ln = lane;
@@ -1944,64 +2016,92 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
     for (int bi = 0; bi < DBLK; ++bi) *reinterpret_cast<f32x4*>(o + 16 * bi) = acc[bi] * inv;
     if (wave == 0 && G == 0) a.part_lse[part] = m_i + __builtin_amdgcn_logf(l);
   }
+  lds_barrier();  // the stages are refilled by the next segment
+  };
+
+  // Segments of this piece: streams from the one holding key r0 on.
+  long long base = base_lo;
+  for (int b = b_lo; b < a.B && base < r1; ++b) {
+    const int L = min(max(a.kv_len[b], 1), a.Lmax);
+    const int lo = a.W > 0 ? max(0, L - a.W) : 0;
+    const int span = L - lo;
+    for (int kvh = 0; kvh < a.Hkv; ++kvh) {
+      const long long s0 = base + (long long)kvh * span, s1 = s0 + span;
+      const long long x0 = max(s0, r0), x1 = min(s1, r1);
+      if (x0 < x1)
+        segment(b, kvh, lo + (int)(x0 - s0), lo + (int)(x1 - s0), b * a.Hkv + kvh + piece);
+    }
+    base += (long long)a.Hkv * span;
+  }
 }
 
-// Log-sum-exp merge of the chunk partials of one (batch, head) and one
-// 64-wide head-dim slice.  256 threads: thread t owns quad t % 16 of the
-// slice and every 16th chunk starting at t / 16; the chunk groups are summed
-// through LDS in a fixed order.
+// Log-sum-exp merge of the segment partials of one (batch, head) and one
+// 64-wide head-dim slice.  The pieces overlapping the head's stream follow
+// from kv_len exactly as k_decode cut them; their partials sit in slots
+// stream + piece.  256 threads: thread t owns quad t % 16 of the slice and
+// every 16th partial starting at t / 16; the groups are summed through LDS
+// in a fixed order.
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_lse, float* __restrict__ out,
-                                                        int nchunks) {
-  // Work-group (query head bh, 64-wide head-dim slice blockIdx.y): 16 quads
-  // of the slice, 16 groups of chunks, so that even a few heads with long
-  // contexts (many chunks) spread over enough work-groups.
+__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __restrict__ out) {
   constexpr int NQ = 16;           // head-dim quads per work-group
-  constexpr int NGRP = 256 / NQ;   // chunk groups
+  constexpr int NGRP = 256 / NQ;   // partial groups
   static_assert(D % (4 * NQ) == 0, "head dim splits into 64-wide slices");
   __shared__ f32x4 snum[NGRP][NQ];
   __shared__ float sden[NGRP][NQ];
   __shared__ float smax[4];
+  __shared__ long long s_red[4];
   const int bh = blockIdx.x;
+  const int b = bh / a.Hq, head = bh % a.Hq, kvh = head / a.g, hg = head % a.g;
   const int qd = threadIdx.x % NQ, grp = threadIdx.x / NQ;
-  const float* lse = part_lse + (size_t)bh * nchunks;
-  // Largest chunk log-sum-exp: a strided share per thread (one load each for
-  // up to 256 chunks), then the wave and work-group maxima.
+  // total keys, and the keys of the streams before this batch entry's
+  long long t = 0, tb = 0;
+  for (int bb = threadIdx.x; bb < a.B; bb += 256) {
+    const long long k = decode_batch_keys(a, bb);
+    t += k;
+    tb += bb < b ? k : 0;
+  }
+  const long long T = block_sum_ll(t, s_red);
+  const long long base_b = block_sum_ll(tb, s_red);
+  const int np = (int)min((long long)a.npieces, max(1LL, T / 64));
+  const long long span = decode_batch_keys(a, b) / a.Hkv;
+  const long long x0 = base_b + (long long)kvh * span, x1 = x0 + span;  // this stream's keys
+  const int p0 = (int)(((x0 + 1) * np - 1) / T), p1 = (int)((x1 * np - 1) / T);  // pieces holding x0, x1 - 1
+  const int npart = p1 - p0 + 1;
+  const size_t first = (size_t)(b * a.Hkv + kvh + p0) * a.g + hg;  // partial k at first + k * (g + ...)
+  auto pidx = [&](int k) { return first + (size_t)k * a.g; };
+  // Largest partial log-sum-exp: a strided share per thread, then the wave
+  // and work-group maxima.
   float M = kNegInf;
-  for (int c = threadIdx.x; c < nchunks; c += 256) M = fmaxf(M, lse[c]);
+  for (int k = threadIdx.x; k < npart; k += 256) M = fmaxf(M, a.part_lse[pidx(k)]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
-  const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (size_t)bh * nchunks * D) + blockIdx.y * NQ + qd;
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + blockIdx.y * NQ + qd;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  // chunks grp, grp + NGRP, ...: four loads in flight per round trip (empty
-  // chunks, lse = -inf, never wrote their partial: their loads are discarded)
+  // partials grp, grp + NGRP, ...: four loads in flight per round trip
   constexpr int U = 4;
-  int c = grp;
-  for (; c + (U - 1) * NGRP < nchunks; c += U * NGRP) {
+  int k = grp;
+  for (; k + (U - 1) * NGRP < npart; k += U * NGRP) {
     f32x4 o[U];
     float e[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      e[u] = lse[c + u * NGRP];
-      o[u] = po[(size_t)(c + u * NGRP) * (D / 4)];
+      e[u] = a.part_lse[pidx(k + u * NGRP)];
+      o[u] = po[pidx(k + u * NGRP) * (D / 4)];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = e[u] == kNegInf ? 0.f : fast_exp2(e[u] - M);
-      num += w * (e[u] == kNegInf ? f32x4{0.f, 0.f, 0.f, 0.f} : o[u]);
+      const float w = fast_exp2(e[u] - M);
+      num += w * o[u];
       den += w;
     }
   }
-  for (; c < nchunks; c += NGRP) {
-    const float e = lse[c];
-    if (e == kNegInf) continue;
-    const float w = fast_exp2(e - M);
-    num += w * po[(size_t)c * (D / 4)];
+  for (; k < npart; k += NGRP) {
+    const float w = fast_exp2(a.part_lse[pidx(k)] - M);
+    num += w * po[pidx(k) * (D / 4)];
     den += w;
   }
   snum[grp][qd] = num;
@@ -2173,22 +2273,15 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   return hipGetLastError();
 }
 
-DecodePlan plan_decode(int B, int Hkv, int W, int max_kv_len) {
-  const long span = W > 0 ? std::min<long>(W, max_kv_len) : max_kv_len;
-  const long streams = (long)B * Hkv;
-  const long target_groups = 2048;
-  long per = (streams * span + target_groups - 1) / target_groups;
-  per = std::max<long>(per, 64);
-  per = std::min<long>(per, 4096);
-  per = (per + 31) / 32 * 32;
+DecodePlan plan_decode(int /*B*/, int /*Hkv*/, int /*W*/, int /*max_kv_len*/) {
   DecodePlan plan;
-  plan.chunk = (int)per;
-  plan.nchunks = (int)((span + per - 1) / per);
+  plan.npieces = kDecodePieces;
   return plan;
 }
 
-size_t decode_workspace(int B, int Hq, int D, const DecodePlan& plan) {
-  const size_t parts = (size_t)B * Hq * plan.nchunks;
+size_t decode_workspace(int B, int Hq, int Hkv, int D, const DecodePlan& plan) {
+  // one partial per (stream + piece) slot and query head of the group
+  const size_t parts = ((size_t)B * Hkv + plan.npieces) * (size_t)(Hq / Hkv);
   return parts * D * sizeof(float) + parts * sizeof(float);
 }
 
@@ -2198,7 +2291,7 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   a.k = static_cast<const uint16_t*>(p.k);
   a.v = static_cast<const uint16_t*>(p.alias ? p.k : p.v);
   a.kv_len = p.kv_len;
-  const size_t parts = (size_t)p.B * p.Hq * p.plan.nchunks;
+  const size_t parts = ((size_t)p.B * p.Hkv + p.plan.npieces) * (size_t)(p.Hq / p.Hkv);
   a.part_o = static_cast<float*>(p.ws);
   a.part_lse = a.part_o + parts * p.D;
   a.B = p.B;
@@ -2207,11 +2300,10 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   a.g = p.Hq / p.Hkv;
   a.Lmax = p.Lmax;
   a.W = p.W;
-  a.nchunks = p.plan.nchunks;
-  a.chunk = p.plan.chunk;
+  a.npieces = p.plan.npieces;
   a.qscale = p.scale * kLog2e;
   fill_rope_rev(&a.rope, p.D, p.theta);
-  const dim3 grid((unsigned)(p.plan.nchunks * p.B * p.Hkv));
+  const dim3 grid((unsigned)p.plan.npieces);
   if (ev.before) (void)hipEventRecord(ev.before, stream);
   if (p.D == 512) {
     if (p.alias)
@@ -2226,11 +2318,9 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   if (p.D == 512)
-    hipLaunchKernelGGL((k_decode_combine<512>), dim3(p.B * p.Hq, 512 / 64), dim3(256), 0, stream, a.part_o,
-                       a.part_lse, p.out, a.nchunks);
+    hipLaunchKernelGGL((k_decode_combine<512>), dim3(p.B * p.Hq, 512 / 64), dim3(256), 0, stream, a, p.out);
   else
-    hipLaunchKernelGGL((k_decode_combine<256>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a.part_o,
-                       a.part_lse, p.out, a.nchunks);
+    hipLaunchKernelGGL((k_decode_combine<256>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a, p.out);
   return hipGetLastError();
 }
 
