@@ -158,7 +158,9 @@ int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t l
  *   kv_len     device int32 [batch], 1 <= kv_len[b] <= max_kv_len <= max_len
  *              (values outside that range give undefined results but no
  *              out-of-bounds access: they are clamped)
- *   max_kv_len host bound on kv_len[], sizes the launch grid
+ *   max_kv_len host bound on kv_len[] (checked against max_len; the split
+ *              of the keys over work-groups is derived from kv_len on the
+ *              device, so it needs no host copy of the lengths)
  *   out        fp32 [batch, Hq, head_dim]
  *   workspace  device scratch of at least gemma4_decode_workspace_bytes()
  */
