@@ -284,6 +284,15 @@ def test_decode_split_invariance():
     assert np.max(np.abs(a[0] - b[0])) < 1e-3
 
 
+def test_decode_repeatable():
+    """Decode has no atomics and merges partials in a fixed order: two calls on
+    the same inputs agree bit for bit."""
+    kw = dict(B=3, Hq=8, Hkv=2, D=512, W=0, alias=False, kv_len=[2000, 37, 4096], Lmax=4096)
+    a = _decode_case("repeat 1", **kw)
+    b = _decode_case("repeat 2", **kw)
+    assert np.array_equal(a, b)
+
+
 def test_workload3_decode():
     w = wl.workloads()[3]
     import torch
