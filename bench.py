@@ -61,32 +61,39 @@ def measured_traffic(kernel):
 
 
 def time_calls(fn, steps, warmup, flush=None):
-    """Average wall time per call (events around each call) and per main kernel (profile events)."""
+    """Average time per call (events around each call) and per main kernel
+    (events the library records immediately around it).  The two are taken on
+    alternating calls, so the call times carry no profiling events of their
+    own."""
     import torch
     from hybrid_sliding_global_amd import _lib
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    tot_call = tot_kern = 0.0
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for quad in evs:  # torch creates the HIP event on first record; the library re-records k0/k1
-        for e in quad:
-            e.record()
-    torch.cuda.synchronize()
-    for i in range(steps):
+
+    def events(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for pair in evs:  # torch creates the HIP event on first record; the library re-records kernel events
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
+        return evs
+
+    calls, kerns = events(steps), events(steps)
+    for (c0, c1), (k0, k1) in zip(calls, kerns):  # interleaved: both see the same clock state
         if flush is not None:
             flush()
-        c0, c1, k0, k1 = evs[i]
-        _lib.set_profile_events(k0, k1)
         c0.record()
         fn()
         c1.record()
+        if flush is not None:
+            flush()
+        _lib.set_profile_events(k0, k1)
+        fn()
         _lib.set_profile_events(None, None)
     torch.cuda.synchronize()
-    for c0, c1, k0, k1 in evs:
-        tot_call += c0.elapsed_time(c1)
-        tot_kern += k0.elapsed_time(k1)
+    tot_call = sum(c0.elapsed_time(c1) for c0, c1 in calls)
+    tot_kern = sum(k0.elapsed_time(k1) for k0, k1 in kerns)
     return tot_call / steps, tot_kern / steps
 
 
