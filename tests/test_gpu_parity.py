@@ -268,6 +268,10 @@ def _decode_case(tag, B, Hq, Hkv, D, W, alias, kv_len, Lmax, seed=0, max_kv_len=
     (2, 2, 2, 256, 0, False, [31, 32], 40),                   # no sharing, tiny lengths
     (1, 4, 1, 256, 1, True, [100], 100),                      # window 1 -> own raw key
     (2, 4, 2, 512, 300, False, [299, 301], 512),              # sliding, separate values, head size 512
+    # 300 short sequences: the batch scan runs over two blocks of 256 entries,
+    # and one piece of the key split covers many whole streams
+    (300, 4, 1, 256, 48, True, [1 + (37 * i) % 97 for i in range(300)], 97),
+    (300, 8, 2, 512, 0, False, [1 + (53 * i) % 60 for i in range(300)], 64),
 ])
 def test_decode_shapes(B, Hq, Hkv, D, W, alias, kv_len, Lmax):
     _decode_case("decode B%d Hq%d Hkv%d D%d W%d alias%d L%s" % (B, Hq, Hkv, D, W, alias, kv_len), B, Hq, Hkv, D, W,
