@@ -546,8 +546,8 @@ k_prefill(PrefillArgs a) {
         }
     };
 
-    // Mask, online softmax and O^T += V^T P^T for key tile j.
-    auto softmax_pv = [&](int j, f32x16 (&s)[MB], const uint16_t* cv) {
+    // Mask and online softmax of key tile j: P^T (bf16, MFMA B-operand order) into pk.
+    auto softmax = [&](int j, f32x16 (&s)[MB], unsigned (&pk)[MB * 8]) {
       const int kbase = j * BN;
       const bool need_mask = (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
       if (need_mask) {
@@ -582,7 +582,6 @@ k_prefill(PrefillArgs a) {
       }
       const float m_use = (m_i == kNegInf) ? 0.f : m_i;
       float rs = 0.f;
-      unsigned pk[MB * 8];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -592,9 +591,10 @@ k_prefill(PrefillArgs a) {
           pk[mb * 8 + rr / 2] = pack_bf16(p0, p1);
         }
       l_i += rs;
-
-      // O^T += V^T P^T.  P^T slot t of key-step kv is key 16*kv + 4*h + t (t < 4)
-      // or 16*kv + 8 + 4*h + (t - 4): the value image stores V in that order.
+    };
+    // O^T += V^T P^T.  P^T slot t of key-step kv is key 16*kv + 4*h + t (t < 4)
+    // or 16*kv + 8 + 4*h + (t - 4): the value image stores V in that order.
+    auto pv = [&](const unsigned (&pk)[MB * 8], const uint16_t* cv) {
       const u32x4* vb = reinterpret_cast<const u32x4*>(cv) + lane;
 #pragma unroll
       for (int kv = 0; kv < KV; ++kv) {
@@ -604,6 +604,60 @@ k_prefill(PrefillArgs a) {
           acc[db] = mfma32(as_bf16x8(vb[(kv * DB + dp * DBW + db) * 64]), pf, acc[db]);
       }
       lds_mfma_pipeline<KV * DBW, kPipeDepth>();
+    };
+    auto softmax_pv = [&](int j, f32x16 (&s)[MB], const uint16_t* cv) {
+      unsigned pk[MB * 8];
+      softmax(j, s, pk);
+      pv(pk, cv);
+    };
+
+    // The same two steps with the operand reads pipelined by hand (a ring of
+    // kPipeDepth reads in flight, the order pinned step by step) and a hook
+    // after every MFMA, which the two-group schedule uses to spread its tile
+    // copies over the MFMAs: issued back to back they hold the wave, and so
+    // its share of the MFMA pipe, until the memory pipeline takes them.
+    auto scores_h = [&](const uint16_t* ck, f32x16 (&s)[MB], auto&& hook) __attribute__((always_inline)) {
+      const u32x4* kb = reinterpret_cast<const u32x4*>(ck) + lane;
+      constexpr int N = MB * KSW;
+      auto kaddr = [&](int t) {
+        const int mb = t / KSW, i = t % KSW;
+        const int ks = i < KSW / 2 ? dp * (KSW / 2) + i : KSTEPS / 2 + dp * (KSW / 2) + (i - KSW / 2);
+        return (mb * KSTEPS + ks) * 64;
+      };
+      u32x4 kr[kPipeDepth];
+#pragma unroll
+      for (int t = 0; t < kPipeDepth; ++t) kr[t] = kb[kaddr(t)];
+#pragma unroll
+      for (int t = 0; t < N; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 kf = as_bf16x8(kr[t % kPipeDepth]);
+        if (t + kPipeDepth < N) kr[t % kPipeDepth] = kb[kaddr(t + kPipeDepth)];
+        const int mb = t / KSW, i = t % KSW;
+        s[mb] = mfma32(kf, qf[i], i == 0 ? f32x16{} : s[mb]);
+        hook(t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pv_h = [&](const unsigned (&pk)[MB * 8], const uint16_t* cv, auto&& hook) __attribute__((always_inline)) {
+      const u32x4* vb = reinterpret_cast<const u32x4*>(cv) + lane;
+      constexpr int N = KV * DBW;
+      u32x4 vr[kPipeDepth];
+#pragma unroll
+      for (int u = 0; u < kPipeDepth; ++u) vr[u] = vb[((u / DBW) * DB + dp * DBW + u % DBW) * 64];
+#pragma unroll
+      for (int t = 0; t < N; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 vf = as_bf16x8(vr[t % kPipeDepth]);
+        if (t + kPipeDepth < N) {
+          const int u = t + kPipeDepth;
+          vr[t % kPipeDepth] = vb[((u / DBW) * DB + dp * DBW + u % DBW) * 64];
+        }
+        const int kv = t / DBW, db = t % DBW;
+        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * kv], pk[4 * kv + 1], pk[4 * kv + 2], pk[4 * kv + 3]});
+        acc[db] = mfma32(vf, pf, acc[db]);
+        hook(t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     if constexpr (DS == 1) {
@@ -631,37 +685,57 @@ k_prefill(PrefillArgs a) {
       // odd u = softmax and PV of tile jb + (u-1)/2.  Key tile j lives in
       // buffer (j - jb) & 1 during phases 2(j-jb) .. 2(j-jb)+1 and value tile
       // j during phases 2(j-jb)+1 .. 2(j-jb)+2; the next key tile is copied
-      // at the start of even phases and the next value tile at the start of
-      // odd ones, each into the buffer its predecessor has just left.
+      // during even phases and the next value tile during odd ones, each
+      // into the buffer its predecessor has just left, spread over the
+      // phase's MFMAs (scores or PV, whichever the wave is running).
       const int grp = wave >> 2;
       const int nt = je - jb + 1;
       auto phase_begin = [&](int t) {
-        // Copies issued at the start of phase t - 1 are first read in phase
-        // t + 1 and may stay in flight; everything older must have landed.
+        // Copies issued during phase t - 1 are first read in phase t + 1 and
+        // may stay in flight; everything older must have landed.
         if (t > 0 && jb + (t - 1) / 2 + 1 <= je)
           wait_vm<LPT>();
         else
           wait_vm<0>();
         lds_barrier();
-        const int jn = jb + t / 2 + 1;
-        if (jn <= je) {
-          if ((t & 1) == 0)
-            issue_k(jn, ((jn - jb) & 1) ? sk1 : sk0);
-          else
-            issue_v(jn, ((jn - jb) & 1) ? sv1 : sv0);
-        }
       };
-      if (grp == 1) phase_begin(0);
+      // The copies of phase t (key tile jn for even t, value tile jn for odd
+      // t, jn = jb + t/2 + 1), one block after every fourth MFMA of the phase.
+      // Past the segment's last tile the copy repeats that tile into the
+      // buffer it would fill (no wave reads it again in this segment), so
+      // every phase issues the same number of copies and the MFMA chains
+      // carry no branches.
+      auto copy_hook = [&](int t) {
+        const int jn = jb + t / 2 + 1;  // decides the buffer, which is free either way
+        const char* src = reinterpret_cast<const char*>(((t & 1) ? vimg : kimg) + (size_t)min(jn, je) * (BN * D));
+        uint16_t* dst = (t & 1) ? (((jn - jb) & 1) ? sv1 : sv0) : (((jn - jb) & 1) ? sk1 : sk0);
+        const unsigned ld = lds_addr(dst) + wave * 1024;
+        return [=](int st) {
+          if (st % 4 == 1) dma_block(src, voff + (st / 4) * NW * 1024, ld + (st / 4) * NW * 1024);
+        };
+      };
+
+      static_assert(MB * KSW >= 4 * LPT && KV * DBW >= 4 * LPT, "each phase's MFMAs must carry its copies");
+      if (grp == 1) {
+        phase_begin(0);
+        const int jn = jb + 1;
+        if (jn <= je) issue_k(jn, sk1);
+      }
       for (int i = 0; i < nt; ++i) {
         f32x16 s[MB];
-        phase_begin(2 * i + grp);
-        scores((i & 1) ? sk1 : sk0, s);
+        const int ta = 2 * i + grp, tb = ta + 1;
+        phase_begin(ta);
+        scores_h((i & 1) ? sk1 : sk0, s, copy_hook(ta));
         publish(s);
-        phase_begin(2 * i + 1 + grp);
+        phase_begin(tb);
+        const uint16_t* cv = (i & 1) ? sv1 : sv0;
         add_partner(s);
-        softmax_pv(jb + i, s, (i & 1) ? sv1 : sv0);
+        unsigned pk[MB * 8];
+        softmax(jb + i, s, pk);
+        pv_h(pk, cv, copy_hook(tb));
       }
       if (grp == 0) phase_begin(2 * nt);
+      wait_vm<0>();  // the repeated copies of the last phases
     }
 
     if (jb != jlo_t || je != jhi_t) {
