@@ -364,7 +364,7 @@ def main():
                    "head_dim": 512, "window": 0, "rope_theta": 1e6, "kv_alias": False,
                    "algorithmic_flops": pre["flops"]},
         "roofline": {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_prefill<512,32,2>")},
+                     "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_prefill<512,32,2,true>")},
     }
     if not args.no_stack:
         log("stack: 35-layer prefill S=2048")

@@ -37,6 +37,7 @@ struct PrefillPlan {
   int BN = 0, ntiles = 0, g = 0, nqt = 0, npair = 0, kpieces = 0;
   int rows = kPrefillRows;  // query rows per tile: 128, or 64 (head size 256, never cut into pieces)
   int paired = 1;  // work unit: 1 = query tiles t and nqt-1-t, 0 = one query tile
+  int split_pv = 0;  // head size 512: PV of a tile split over two phases (long segments)
   size_t kimg_bytes = 0, vimg_off = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0,
          total = 0;
 };

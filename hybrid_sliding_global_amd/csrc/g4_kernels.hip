@@ -386,7 +386,10 @@ __device__ __forceinline__ float max_lane_pair(float x) {  // max over lanes l a
 // Flash-style prefill.  DS = number of waves sharing one 32-row query group,
 // each owning 1/DS of the head dimension (DS = 2 for head size 512 keeps
 // the 32 x 512 fp32 output block of a row group in two waves'
-// accumulators).  A work-group is 4 * DS waves and covers one 128-row query
+// accumulators).  SPV (DS = 2) picks the tile schedule: PV of a tile in its
+// softmax phase (false), or split between that phase and the next score
+// phase (true: shorter critical path, longer pipeline start; for long
+// segments).  A work-group is 4 * DS waves and covers one 128-row query
 // tile of one (batch, kv-head) at a time.
 //
 // Work split: the query tiles of a (batch, kv-head) are paired long with
@@ -397,7 +400,7 @@ __device__ __forceinline__ float max_lane_pair(float x) {  // max over lanes l a
 // partial (O, running max, running sum) and bumps the tile's counter; the
 // last one merges the others into its own registers and writes the output.
 // Nobody waits for anybody.
-template <int D, int BN, int DS>
+template <int D, int BN, int DS, bool SPV>
 __global__ __attribute__((amdgpu_flat_work_group_size(256 * DS, 256 * DS), amdgpu_waves_per_eu(DS, DS))) void
 k_prefill(PrefillArgs a) {
   constexpr int NT = 256 * DS;                // threads
@@ -547,7 +550,7 @@ k_prefill(PrefillArgs a) {
     };
 
     // Mask and online softmax of key tile j: P^T (bf16, MFMA B-operand order) into pk.
-    auto softmax = [&](int j, f32x16 (&s)[MB], unsigned (&pk)[MB * 8]) {
+    auto softmax = [&](int j, f32x16 (&s)[MB], unsigned (&pk)[MB * 8]) __attribute__((always_inline)) {
       const int kbase = j * BN;
       const bool need_mask = (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
       if (need_mask) {
@@ -638,7 +641,24 @@ k_prefill(PrefillArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto pv_h = [&](const unsigned (&pk)[MB * 8], const uint16_t* cv, auto&& hook) __attribute__((always_inline)) {
+    // O^T += V^T P^T for the 16-key step kv only (DBW MFMAs).
+    auto pv_kv = [&](auto kv_c, const u32x4& pf, const uint16_t* cv, auto&& hook) __attribute__((always_inline)) {
+      constexpr int kv = decltype(kv_c)::value;
+      const u32x4* vb = reinterpret_cast<const u32x4*>(cv) + lane + (kv * DB + dp * DBW) * 64;
+      u32x4 vr[kPipeDepth];
+#pragma unroll
+      for (int u = 0; u < kPipeDepth; ++u) vr[u] = vb[u * 64];
+#pragma unroll
+      for (int t = 0; t < DBW; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 vf = as_bf16x8(vr[t % kPipeDepth]);
+        if (t + kPipeDepth < DBW) vr[t % kPipeDepth] = vb[(t + kPipeDepth) * 64];
+        acc[t] = mfma32(vf, as_bf16x8(pf), acc[t]);
+        hook(t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pv_hd = [&](const unsigned (&pk)[MB * 8], const uint16_t* cv, auto&& hook) __attribute__((always_inline)) {
       const u32x4* vb = reinterpret_cast<const u32x4*>(cv) + lane;
       constexpr int N = KV * DBW;
       u32x4 vr[kPipeDepth];
@@ -676,6 +696,133 @@ k_prefill(PrefillArgs a) {
         if (++j > je) break;
       }
     } else {
+      if constexpr (SPV) {
+      // Two wave groups (waves 0-3 and 4-7, one of each per SIMD) run the
+      // same tile sequence half a step apart.  A group's step on tile i has
+      // two phases: (A) O^T += V^T P^T for tile i-1, then the partial scores
+      // of tile i; (B) the partner's half of the scores and the softmax of
+      // tile i for this wave's 16 keys.  Phase t: group g works on u = t - g
+      // (even u: phase A of tile jb + u/2, odd u: phase B of tile
+      // jb + (u-1)/2); after the last tile one more phase A holds only its
+      // PV.  In every phase one wave of each SIMD runs 32 MFMAs while the
+      // other adds its partner's scores and runs the softmax.
+      //
+      // LDS exchange slot sx[w] of wave w: its partial scores of tile i
+      // (written in phase A of tile i, read by the partner in phase B), then
+      // the partner's probabilities of tile i (written by the partner in
+      // phase B after reading the scores, read by w in the next phase A
+      // before it writes its next scores there).
+      //
+      // Copies: at every even phase t < 2 nt each wave copies its share of
+      // key tile t/2 + 1 and value tile max(t/2, 1) (relative to jb) into
+      // the buffers their predecessors two tiles back have left (key tile j
+      // is read in phases 2j .. 2j+1, value tile j in 2j+2 .. 2j+3), so every
+      // copy has two phases to land.  A tile past the segment's end is
+      // replaced by its last tile (its buffer is free and never read again
+      // in the segment), so every even phase issues the same 2 * LPT copies.
+      // Phase-A waves spread them over their MFMAs; phase-B waves issue them
+      // at the start of the phase.
+      static_assert(MB == 1 && KV == 2, "one 32-key block per tile");
+      const int grp = wave >> 2;
+      const int nt = je - jb + 1;
+      // Copies of phase t: even t, key tile t/2 + 1 (LPT blocks) and the
+      // second 16-key half of value tile t/2 (LPT/2 blocks); odd t, the
+      // first half of value tile (t+1)/2 (LPT/2 blocks); none from 2 nt on.
+      // A value tile's first half is read in phase B of its tile, its
+      // second half in the next phase A, so each half has its own two-phase
+      // window and every copy has two phases to land.
+      auto ncopies = [&](int t) { return (t < 0 || t >= 2 * nt) ? 0 : ((t & 1) ? LPT / 2 : LPT + LPT / 2); };
+      auto phase_begin = [&](int t) {
+        // Copies issued during phase t - 1 are first read in phase t + 1 and
+        // may stay in flight; everything older must have landed.
+        const int n = ncopies(t - 1);
+        if (n == LPT + LPT / 2)
+          wait_vm<LPT + LPT / 2>();
+        else if (n == LPT / 2)
+          wait_vm<LPT / 2>();
+        else
+          wait_vm<0>();
+        lds_barrier();
+      };
+      // Block c (< ncopies(t)) of this wave's copies of phase t.
+      auto copy_blk = [&](int t, int c) {
+        bool isv;
+        int jr, u;
+        if (t & 1) {
+          isv = true, jr = (t + 1) / 2, u = c;  // value blocks wave + u NW, u < LPT/2: first half
+        } else if (c < LPT) {
+          isv = false, jr = t / 2 + 1, u = c;
+        } else {
+          isv = true, jr = t / 2, u = LPT / 2 + (c - LPT);  // second half
+        }
+        const char* src = reinterpret_cast<const char*>((isv ? vimg : kimg) + (size_t)min(jb + jr, je) * (BN * D));
+        uint16_t* dst = isv ? ((jr & 1) ? sv1 : sv0) : ((jr & 1) ? sk1 : sk0);
+        dma_block(src, voff + u * NW * 1024, lds_addr(dst) + wave * 1024 + u * NW * 1024);
+      };
+      auto copy_all = [&](int t) {
+#pragma unroll
+        for (int c = 0; c < LPT + LPT / 2; ++c) copy_blk(t, c);
+      };
+      static_assert(LPT == 4 && DBW == 8 && KSW == 16, "copy hooks below assume this tile split");
+      using K0 = std::integral_constant<int, 0>;
+      using K1 = std::integral_constant<int, 1>;
+      auto run = [&](auto g_c) __attribute__((always_inline)) {
+        constexpr int G = decltype(g_c)::value;
+        unsigned pk[MB * 8];
+        f32x16 s[MB];
+        if (G == 1) {
+          phase_begin(0);
+          copy_all(0);
+        }
+        phase_begin(G);  // phase A of tile 0: scores only
+        if (G == 0)
+          scores_h(sk0, s, [&](int st) { if (st % 2 == 1 && st / 2 < 6) copy_blk(0, st / 2); });
+        else
+          scores_h(sk0, s, [&](int st) { if (st % 4 == 1 && st / 4 < 2) copy_blk(1, st / 4); });
+        publish(s);
+        // Phase B of tile i: the partner's scores, the softmax, the PV of the
+        // first 16-key step; then the barrier that opens phase A of tile i + 1.
+        auto phase_b = [&](int i, auto copies_c) __attribute__((always_inline)) {
+          const int tb = 2 * i + 1 + G;
+          phase_begin(tb);
+          add_partner(s);
+          softmax(jb + i, s, pk);
+          const u32x4 pf0{pk[0], pk[1], pk[2], pk[3]};
+          if constexpr (!decltype(copies_c)::value)
+            pv_kv(K0{}, pf0, (i & 1) ? sv1 : sv0, [](int) {});
+          else if constexpr (G == 1)  // even phase: six copies
+            pv_kv(K0{}, pf0, (i & 1) ? sv1 : sv0, [&](int st) { if (st < 6) copy_blk(tb, st); });
+          else  // odd phase: two copies
+            pv_kv(K0{}, pf0, (i & 1) ? sv1 : sv0, [&](int st) { if (st % 4 == 1) copy_blk(tb, st / 4); });
+          phase_begin(tb + 1);
+        };
+        for (int i = 0; i + 1 < nt; ++i) {
+          phase_b(i, std::true_type{});
+          const int ta = 2 * i + 2 + G;
+          const u32x4 pf1{pk[4], pk[5], pk[6], pk[7]};
+          const uint16_t* cv = (i & 1) ? sv1 : sv0;
+          if (G == 0) {  // even phase: six copies
+            pv_kv(K1{}, pf1, cv, [&](int st) { if (st % 4 == 1) copy_blk(ta, st / 4); });
+            scores_h(((i + 1) & 1) ? sk1 : sk0, s, [&](int st) { if (st % 4 == 1) copy_blk(ta, 2 + st / 4); });
+          } else {  // odd phase: two copies
+            pv_kv(K1{}, pf1, cv, [&](int st) { if (st % 4 == 1) copy_blk(ta, st / 4); });
+            scores_h(((i + 1) & 1) ? sk1 : sk0, s, [](int) {});
+          }
+          publish(s);
+        }
+        if (G == 0)
+          phase_b(nt - 1, std::true_type{});  // phase 2 nt - 1: two copies (past the end)
+        else
+          phase_b(nt - 1, std::false_type{});
+        pv_kv(K1{}, u32x4{pk[4], pk[5], pk[6], pk[7]}, ((nt - 1) & 1) ? sv1 : sv0, [](int) {});
+        if (G == 0) phase_begin(2 * nt + 1);
+      };
+      if (grp == 0)
+        run(std::integral_constant<int, 0>{});
+      else
+        run(std::integral_constant<int, 1>{});
+      wait_vm<0>();
+      } else {
       // Two wave groups (waves 0-3 and 4-7, one of each per SIMD) run the
       // same tile sequence half a step apart: in every phase one group
       // computes scores for tile i while the other finishes tile i-1
@@ -732,10 +879,11 @@ k_prefill(PrefillArgs a) {
         add_partner(s);
         unsigned pk[MB * 8];
         softmax(jb + i, s, pk);
-        pv_h(pk, cv, copy_hook(tb));
+        pv_hd(pk, cv, copy_hook(tb));
       }
       if (grp == 0) phase_begin(2 * nt);
       wait_vm<0>();  // the repeated copies of the last phases
+      }
     }
 
     if (jb != jlo_t || je != jhi_t) {
@@ -2222,6 +2370,7 @@ static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int rows, int
 // (query load and rotation, first tile copy, output) and, when a tile is
 // split, the partial-result store and merge; the constants are per-kernel
 // cycle counts measured on MI355X.
+constexpr int kSplitPvMinTiles = 32;
 struct PrefillCosts {
   double tile, segment, split;
 };
@@ -2240,6 +2389,15 @@ static int prefill_rows_override() {
   return (v == 64 || v == 128) ? v : 0;
 }
 
+// G4_PREFILL_SPLIT_PV=0 or 1 pins the head-size-512 schedule (tests use it
+// to reach both at small sizes); unset = by key tiles per work-group.
+static int prefill_split_pv_override() {
+  const char* e = std::getenv("G4_PREFILL_SPLIT_PV");
+  if (!e) return -1;
+  const int v = std::atoi(e);
+  return (v == 0 || v == 1) ? v : -1;
+}
+
 PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   PrefillPlan p;
   p.BN = prefill_key_tile(D);
@@ -2247,6 +2405,7 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   p.g = Hq / Hkv;
   const int forced = D == 256 ? prefill_rows_override() : 0;
   double best = 0.0;
+  int best_tiles = 0;
   for (int rows : {128, 64}) {
     if (rows == 64 && D != 256) continue;
     if (forced && rows != forced) continue;
@@ -2280,10 +2439,17 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
           p.paired = paired;
           p.npair = nunits;
           p.kpieces = k;
+          best_tiles = (int)std::ceil((double)umax / k);
         }
       }
     }
   }
+  // The split-PV schedule of the head-size-512 kernel costs one more phase
+  // and a longer pipeline start per segment and saves about 5 % per key
+  // tile; it pays from about 32 key tiles per work-group on (measured:
+  // faster at 65 tiles, slower at 16).
+  const int spv = prefill_split_pv_override();
+  p.split_pv = D == 512 && (spv >= 0 ? spv == 1 : best_tiles >= kSplitPvMinTiles) ? 1 : 0;
   const long groups = (long)B * Hkv * p.npair;
   p.kimg_bytes = (size_t)B * Hkv * p.ntiles * p.BN * D * 2;
   p.vimg_off = (p.kimg_bytes + 255) / 256 * 256;
@@ -2333,7 +2499,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
     hipLaunchKernelGGL((k_prefill_prep<512, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
-    hipLaunchKernelGGL((k_prefill<512, 32, 2>), grid_a, dim3(512), 0, stream, a);
+    if (pl.split_pv)
+      hipLaunchKernelGGL((k_prefill<512, 32, 2, true>), grid_a, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_prefill<512, 32, 2, false>), grid_a, dim3(512), 0, stream, a);
   } else {
     hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);

@@ -86,6 +86,23 @@ def test_prefill_shapes(B, S, Hq, Hkv, D, W, alias, Lmax):
                   alias, Lmax)
 
 
+@pytest.mark.parametrize("split_pv", [0, 1])
+@pytest.mark.parametrize("B,S,Hq,Hkv,W,alias,Lmax", [
+    (1, 200, 8, 2, 0, False, 256),      # ragged S, poisoned rows past S
+    (1, 77, 6, 2, 0, False, 77),        # GQA group of 3
+    (1, 1, 4, 1, 0, False, 1),          # single token: one key tile
+    (1, 300, 4, 4, 64, True, 300),      # windowed, K=V
+    (1, 640, 8, 2, 0, False, 640),      # pairs cut into pieces
+    (2, 1100, 8, 2, 0, False, 1100),    # two sequences, long segments
+    (1, 37, 160, 1, 0, False, 40),      # GQA group of 160
+])
+def test_prefill_head512_schedules(monkeypatch, split_pv, B, S, Hq, Hkv, W, alias, Lmax):
+    """Head size 512 has two tile schedules (PV in one phase, or split over two); both against the oracle."""
+    monkeypatch.setenv("G4_PREFILL_SPLIT_PV", str(split_pv))
+    _prefill_case("prefill splitpv%d B%d S%d Hq%d Hkv%d W%d alias%d" % (split_pv, B, S, Hq, Hkv, W, alias), B, S, Hq,
+                  Hkv, 512, W, alias, Lmax)
+
+
 @pytest.mark.parametrize("rows", [64, 128])
 @pytest.mark.parametrize("B,S,Hq,Hkv,W,alias,Lmax", [
     (2, 333, 8, 1, 48, True, 333),      # sliding K=V, batch 2, ragged
