@@ -2258,16 +2258,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 }
 
 // Log-sum-exp merge of the segment partials of one (batch, head) and one
-// 64-wide head-dim slice.  The pieces overlapping the head's stream follow
-// from kv_len exactly as k_decode cut them; their partials sit in slots
-// stream + piece.  256 threads: thread t owns quad t % 16 of the slice and
-// every 16th partial starting at t / 16; the groups are summed through LDS
-// in a fixed order.
-template <int D>
+// slice of NQ head-dim quads (blockIdx.y; NQ = D/4: the whole head).  The
+// pieces overlapping the head's stream follow from kv_len exactly as
+// k_decode cut them; their partials sit in slots stream + piece.  256
+// threads: thread t owns quad t % NQ and every (256/NQ)-th partial from
+// t / NQ on; its first four partials load together with the log-sum-exps,
+// the rest four at a time, and the groups are summed through LDS in a
+// fixed order.  Wide slices suit streams of few pieces (one work-group per
+// head, one memory round trip), narrow ones streams of many (more
+// partials in flight).
+template <int D, int NQ>
 __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __restrict__ out) {
-  constexpr int NQ = 16;           // head-dim quads per work-group
-  constexpr int NGRP = 256 / NQ;   // partial groups
-  static_assert(D % (4 * NQ) == 0, "head dim splits into 64-wide slices");
+  constexpr int NGRP = 256 / NQ;    // partial groups
+  constexpr int U = 4;              // partials per thread loaded before the maximum is known
+  static_assert(NGRP * NQ == 256, "one thread per (partial group, quad)");
   __shared__ f32x4 snum[NGRP][NQ];
   __shared__ float sden[NGRP][NQ];
   __shared__ float smax[4];
@@ -2289,10 +2293,20 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __r
   const long long x0 = base_b + (long long)kvh * span, x1 = x0 + span;  // this stream's keys
   const int p0 = (int)(((x0 + 1) * np - 1) / T), p1 = (int)((x1 * np - 1) / T);  // pieces holding x0, x1 - 1
   const int npart = p1 - p0 + 1;
-  const size_t first = (size_t)(b * a.Hkv + kvh + p0) * a.g + hg;  // partial k at first + k * (g + ...)
+  const size_t first = (size_t)(b * a.Hkv + kvh + p0) * a.g + hg;  // partial k at first + k * g
   auto pidx = [&](int k) { return first + (size_t)k * a.g; };
-  // Largest partial log-sum-exp: a strided share per thread, then the wave
-  // and work-group maxima.
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + blockIdx.y * NQ + qd;
+  // This thread's first U partials (grp, grp + NGRP, ...) are loaded before
+  // the largest log-sum-exp is known, so both take one memory round trip.
+  f32x4 o[U];
+  float e[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = grp + u * NGRP;
+    const bool in = k < npart;
+    e[u] = in ? a.part_lse[pidx(k)] : kNegInf;
+    o[u] = in ? po[pidx(k) * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float M = kNegInf;
   for (int k = threadIdx.x; k < npart; k += 256) M = fmaxf(M, a.part_lse[pidx(k)]);
 #pragma unroll
@@ -2300,15 +2314,16 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __r
   if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
-  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + blockIdx.y * NQ + qd;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  // partials grp, grp + NGRP, ...: four loads in flight per round trip
-  constexpr int U = 4;
-  int k = grp;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float w = e[u] == kNegInf ? 0.f : fast_exp2(e[u] - M);
+    num += w * o[u];
+    den += w;
+  }
+  int k = grp + U * NGRP;  // streams cut into more pieces: four loads in flight per round trip
   for (; k + (U - 1) * NGRP < npart; k += U * NGRP) {
-    f32x4 o[U];
-    float e[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       e[u] = a.part_lse[pidx(k + u * NGRP)];
@@ -2516,6 +2531,11 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   return hipGetLastError();
 }
 
+// Average partials per stream up to which the merge takes a whole head per
+// work-group (its threads then hold 2 (head size 512) or 4 (256) groups
+// of four partials in flight).
+constexpr int kCombineWideMaxParts = 8;
+
 DecodePlan plan_decode(int /*B*/, int /*Hkv*/, int /*W*/, int /*max_kv_len*/) {
   DecodePlan plan;
   plan.npieces = kDecodePieces;
@@ -2560,10 +2580,19 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
       hipLaunchKernelGGL((k_decode<256, false, kDecodeStages>), grid, dim3(256), 0, stream, a);
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
-  if (p.D == 512)
-    hipLaunchKernelGGL((k_decode_combine<512>), dim3(p.B * p.Hq, 512 / 64), dim3(256), 0, stream, a, p.out);
-  else
-    hipLaunchKernelGGL((k_decode_combine<256>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a, p.out);
+  // Streams of few pieces: one work-group per head; of many: 64-wide slices.
+  const bool wide = p.plan.npieces / (p.B * p.Hkv) + 1 <= kCombineWideMaxParts;
+  if (p.D == 512) {
+    if (wide)
+      hipLaunchKernelGGL((k_decode_combine<512, 128>), dim3(p.B * p.Hq), dim3(256), 0, stream, a, p.out);
+    else
+      hipLaunchKernelGGL((k_decode_combine<512, 16>), dim3(p.B * p.Hq, 512 / 64), dim3(256), 0, stream, a, p.out);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((k_decode_combine<256, 64>), dim3(p.B * p.Hq), dim3(256), 0, stream, a, p.out);
+    else
+      hipLaunchKernelGGL((k_decode_combine<256, 16>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a, p.out);
+  }
   return hipGetLastError();
 }
 
