@@ -305,6 +305,17 @@ def test_decode_split_invariance():
     assert np.max(np.abs(a[0] - b[0])) < 1e-3
 
 
+@pytest.mark.parametrize("split_pv", [0, 1])
+def test_prefill_head512_repeatable(monkeypatch, split_pv):
+    """Tiles cut into pieces are merged by whichever piece arrives last, in
+    ascending piece order: two calls agree bit for bit under both schedules."""
+    monkeypatch.setenv("G4_PREFILL_SPLIT_PV", str(split_pv))
+    kw = (1, 640, 8, 2, 512, 0, False, 640)
+    a = _prefill_case("repeat 1 splitpv%d" % split_pv, *kw)
+    b = _prefill_case("repeat 2 splitpv%d" % split_pv, *kw)
+    assert np.array_equal(a, b)
+
+
 def test_decode_repeatable():
     """Decode has no atomics and merges partials in a fixed order: two calls on
     the same inputs agree bit for bit."""
