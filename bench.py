@@ -168,6 +168,70 @@ def cpu_baseline(pre, budget_s=15.0):
                       "fp64, %.2f s per pass, %d pass(es)" % (n, dt, reps)}
 
 
+def make_flush():
+    """A call that evicts L2 and the 256 MB MALL by reading (not writing) a
+    512 MiB buffer, so the next timed kernel starts from HBM and no dirty
+    lines of the flush are written back inside it."""
+    import torch
+    buf = torch.ones(1 << 27, dtype=torch.float32, device="cuda:0")  # 512 MiB
+    sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def flush():
+        torch.sum(buf, dim=0, out=sink)
+
+    return flush
+
+
+def bench_hbm_reference(reps=10):
+    """Rates of plain library kernels on this GPU, as context for the decode
+    roofline: torch's device copy of 2 GiB (read + write bytes) and torch's sum
+    over 2 GiB (read bytes)."""
+    import torch
+    n = 1 << 31
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+    res = {}
+    for tag, fn, nbytes in (("copy", lambda: dst.copy_(src), 2 * n), ("read", lambda: torch.sum(src, dim=0, out=sink), n)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[tag + "_GB/s"] = nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    return res
+
+
+def bench_small_prefill(steps, warmup):
+    """The single sliding-layer prefill (B=1, S=64, Hq=4, Hkv=1, D=256, W=32,
+    K=V): a latency-bound correctness workload, timed per call."""
+    import torch
+    from hybrid_sliding_global_amd import Stack, inputs
+    from hybrid_sliding_global_amd import workloads as wl
+    w = wl.workloads()[1]
+    d = w.layers[0]
+    q = dev(inputs.normal_bf16([1, 0, inputs.TENSOR_Q], (1, 64, 4, 256)))
+    k = dev(inputs.normal_bf16([1, 0, inputs.TENSOR_K], (1, 1, 64, 256)))
+    st = Stack(w.layers)
+    out = torch.empty((1, 64, 4, 256), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(st.prefill_workspace_bytes(0, 1, 64), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        st.prefill(0, q, [k], [None], out=out, workspace=ws)
+
+    call_ms, kern_ms = time_calls(step, steps, warmup)
+    flops = wl.prefill_flops(64, 4, 256, d["window"])
+    return {"workload": "sliding_prefill_s64", "algorithmic_flops": flops, "ms_per_call": call_ms,
+            "kernel_ms": kern_ms, "TFLOP/s": flops / (call_ms * 1e-3) / 1e12,
+            "note": "latency-bound: a few microseconds of launch and set-up for 6.4 MFLOP"}
+
+
 def bench_decode(steps, warmup):
     import torch
     from hybrid_sliding_global_amd import Stack, inputs
@@ -176,11 +240,7 @@ def bench_decode(steps, warmup):
     B, L = w.batch, w.kv_len
     kv = np.full(B, L, np.int32)
     kl = torch.from_numpy(kv).to("cuda:0")
-    flush_buf = torch.empty(1 << 29, dtype=torch.uint8, device="cuda:0")  # 512 MiB > the 256 MB MALL
-
-    def flush():
-        flush_buf.fill_(1)
-
+    flush = make_flush()
     res = {}
     total_bytes = 0
     total_ms = 0.0
@@ -226,11 +286,7 @@ def bench_decode_long(steps, warmup):
     kv = inputs.kv_lengths_uniform([5, 0, inputs.TENSOR_LEN], B, w.kv_len_range[0], w.kv_len_range[1])
     kl = torch.from_numpy(kv).to("cuda:0")
     max_kv = int(kv.max())
-    flush_buf = torch.empty(1 << 29, dtype=torch.uint8, device="cuda:0")  # 512 MiB > the 256 MB MALL
-
-    def flush():
-        flush_buf.fill_(1)
-
+    flush = make_flush()
     res = {}
     for li, d in enumerate(w.layers):
         D, Hq, Hkv = d["head_dim"], d["num_q_heads"], d["num_kv_heads"]
@@ -330,6 +386,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-long-decode", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--no-hbm-reference", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -383,6 +441,14 @@ def main():
         log("decode long: full-layer kernel %.1f GB/s, sliding-layer kernel %.1f GB/s" %
             (line["long_decode"]["layers"]["full"]["kernel_GB/s"],
              line["long_decode"]["layers"]["sliding"]["kernel_GB/s"]))
+    if not args.no_small:
+        log("small prefill: S=64 sliding layer")
+        line["small_prefill"] = bench_small_prefill(max(10, args.steps), args.warmup)
+        log("small prefill: %.1f us per call" % (line["small_prefill"]["ms_per_call"] * 1e3))
+    if not args.no_hbm_reference:
+        log("hbm reference: torch copy and sum over 2 GiB")
+        line["hbm_reference"] = bench_hbm_reference()
+        log("hbm reference: %s" % json.dumps(line["hbm_reference"]))
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on sampled rows")
         line["cpu_baseline"] = cpu_baseline(pre)

@@ -159,11 +159,24 @@ def _ptr_table(ts):
     return arr
 
 
-def _stream(stream) -> Optional[int]:
+def _resolve_stream(stream):
+    """The torch stream a call launches on: the given one, else the current one."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _alloc_on(stream, shape, dtype, device):
+    """A temporary allocated for use on ``stream``.
+
+    torch's caching allocator ties a block to the stream that was current
+    when it was allocated and hands it out again as soon as the tensor is
+    freed, ordered only against that stream.  Allocating under the launch
+    stream keeps a block freed on return from being reused while the kernels
+    enqueued on that stream may still read or write it.
+    """
+    import torch
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _check_tensor(t, name, dtype, shape):
@@ -217,17 +230,18 @@ class Stack:
         _check_tensor(k, "k_cache", torch.bfloat16, (B, d["num_kv_heads"], Lmax, d["head_dim"]))
         if not d["kv_alias"]:
             _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
+        s = _resolve_stream(stream)
         if out is None:
-            out = torch.empty((B, S, Hq, D), dtype=torch.float32, device=q.device)
+            out = _alloc_on(s, (B, S, Hq, D), torch.float32, q.device)
         _check_tensor(out, "out", torch.float32, (B, S, Hq, D))
         need = self.prefill_workspace_bytes(layer, B, S)
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc_on(s, (need,), torch.uint8, q.device)
         kt = _ptr_table(list(k_caches))
         vt = _ptr_table(list(v_caches)) if v_caches is not None else None
         _check(load().gemma4_attn_prefill(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax, _ptr(out),
                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                          _stream(stream)))
+                                          int(s.cuda_stream)))
         return out
 
     def decode(self, layer: int, q, k_caches, v_caches, kv_len, max_kv_len: int, out=None, workspace=None,
@@ -246,15 +260,16 @@ class Stack:
         if not d["kv_alias"]:
             _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
         _check_tensor(kv_len, "kv_len", torch.int32, (B,))
+        s = _resolve_stream(stream)
         if out is None:
-            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+            out = _alloc_on(s, (B, Hq, D), torch.float32, q.device)
         _check_tensor(out, "out", torch.float32, (B, Hq, D))
         need = self.decode_workspace_bytes(layer, B, max_kv_len)
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc_on(s, (need,), torch.uint8, q.device)
         kt = _ptr_table(list(k_caches))
         vt = _ptr_table(list(v_caches)) if v_caches is not None else None
         _check(load().gemma4_attn_decode(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
                                          int(max_kv_len), _ptr(out), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+                                         workspace.numel() * workspace.element_size(), int(s.cuda_stream)))
         return out

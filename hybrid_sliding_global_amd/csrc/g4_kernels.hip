@@ -60,6 +60,7 @@ constexpr float kMaxGrowth = 64.f;     // log2 units: largest P = 2^(s - referen
 #define G4_PIPE_DEPTH 4
 #endif
 constexpr int kDecodePieces = 512;   // decode work-groups: two per CU of an MI355X
+constexpr int kReanchorSteps = 64;     // decode: query rotation recomputed from the fp64 angle every 64 key steps
 constexpr int kDecodeStages = 4;      // 16-row key/value stages in the decode LDS ring (2 when K and V
                                       // are both staged at head size 512, so two work-groups share a CU)
 
@@ -2091,31 +2092,43 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
       kcs[kk][2 * t + 1] = __builtin_amdgcn_sinf(x);
     }
   // Query side: u = RoPE(q, P - k_start) * scale * log2(e) in fp32 (fp64
-  // angle), and the per-step rotation R_{-16}.
+  // angle), and the per-step rotation R_{-16}.  The recurrence u <- R_{-16} u
+  // is re-anchored from the fp64 angle every kReanchorSteps steps, so its
+  // fp32 drift (angle and length) is bounded whatever the segment length.
   float ux[KH][8], uy[KH][8], stc[KH][8], sts[KH][8];
+  u32x4 qx[KH], qy[KH];  // raw query pairs (bf16) of this lane
   {
     const uint16_t* qrow = a.q + ((size_t)b * a.Hq + head) * D;
-    const double rel = (double)(L - 1 - k_start);
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int d0 = wave * FQ + 32 * kk + 8 * G;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
-      const u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+      qx[kk] = *reinterpret_cast<const u32x4*>(qrow + d0);
+      qy[kk] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        float sn, cn;
-        sincos_rev(rel, a.rope.rev[d0 + t], sn, cn);
         float st = (float)KPS * (float)a.rope.rev[d0 + t];
         st -= __builtin_rintf(st);
-        const float xa = (t & 1) ? bf_hi(x[t >> 1]) : bf_lo(x[t >> 1]);
-        const float ya = (t & 1) ? bf_hi(y[t >> 1]) : bf_lo(y[t >> 1]);
-        ux[kk][t] = qvalid ? (xa * cn - ya * sn) * a.qscale : 0.f;
-        uy[kk][t] = qvalid ? (ya * cn + xa * sn) * a.qscale : 0.f;
         stc[kk][t] = __builtin_amdgcn_cosf(st);
         sts[kk][t] = -__builtin_amdgcn_sinf(st);  // rotation by -KPS positions
       }
     }
   }
+  auto anchor = [&](double rel) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      const int d0 = wave * FQ + 32 * kk + 8 * G;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float sn, cn;
+        sincos_rev(rel, a.rope.rev[d0 + t], sn, cn);
+        const float xa = (t & 1) ? bf_hi(qx[kk][t >> 1]) : bf_lo(qx[kk][t >> 1]);
+        const float ya = (t & 1) ? bf_hi(qy[kk][t >> 1]) : bf_lo(qy[kk][t >> 1]);
+        ux[kk][t] = qvalid ? (xa * cn - ya * sn) * a.qscale : 0.f;
+        uy[kk][t] = qvalid ? (ya * cn + xa * sn) * a.qscale : 0.f;
+      }
+    }
+  };
+  anchor((double)(L - 1 - k_start));
 
   f32x4 acc[DBLK];
 #pragma unroll
@@ -2124,6 +2137,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 
   for (int s = 0; s < nsteps; ++s) {
     const int stg = s % NSTAGE;
+    if (s > 0 && s % kReanchorSteps == 0) anchor((double)(L - 1 - k_start - s * KPS));
     // Q' for this step (bf16), then advance u by R_{-16} for the next one.
     bf16x8 qf[KSTEPS];
 #pragma unroll

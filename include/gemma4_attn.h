@@ -3,23 +3,25 @@
  * attention library (libgemma4_attn.so).
  *
  * The layer this library computes is the attention core of a Gemma-4-style
- * decoder stack:
- *   - sliding-window layers with head size 256 and full-attention layers
- *     with head size 512 on every fifth layer, each with its own RoPE theta
- *     (1e4 sliding, 1e6 full), and 35 layers that read only 15 distinct KV
- *     caches -- onnxruntime-genai feature request "Support for Google Gemma 4
- *     model family (PLE architecture, variable head dims, KV cache sharing)",
- *     sections "Variable Attention Head Dimensions", "KV Cache Sharing",
- *     "Gemma 4 Model Details" and "What Would Need to Change" (per-layer head
- *     size, a KV sharing map, per-layer cache buffers);
- *   - K=V aliasing in sliding layers, where one projection serves as both
- *     key and value -- Gemma-4 weight loader page
- *     (spark_model/weight_loader/gemma4.rs), comment in supports_tp; SGLang
- *     PR "Support encoder-free unified Text/Vision/Audio model",
- *     attention_k_eq_v;
- *   - an attention operator that receives the RoPE and KV-cache parameters
- *     directly -- Hugging Face forum post "Contributing Gemma 4 support and
- *     ONNX export optimizations", ONNX tracing item on sdpa_attention_forward.
+ * decoder stack.  Citations below name the page and its section:
+ *
+ *   [FR] onnxruntime-genai feature request "Support for Google Gemma 4 model
+ *        family (PLE architecture, variable head dims, KV cache sharing)":
+ *        "Three Architectural Blockers" (2. Variable Attention Head
+ *        Dimensions, 3. KV Cache Sharing), "Gemma 4 Model Details", "What
+ *        Would Need to Change" (items 1 Builder, 2 Runtime, 3 Config);
+ *   [HF] Hugging Face forum post "Contributing Gemma 4 support and ONNX
+ *        export optimizations", "Key Technical Contributions", item "ONNX
+ *        Tracing Compatibility (GQA & MoE Attention)" (sdpa_attention_forward
+ *        handing an attention operator its dual-RoPE and KV-cache
+ *        parameters);
+ *   [LD] Gemma-4 weight loader source page (spark_model/weight_loader/
+ *        gemma4.rs): module comment, supports_tp comment, load_layers
+ *        (layer_kv_dtypes), kv_layer_dims;
+ *   [SG] SGLang pull request "[Model] Support encoder-free unified
+ *        Text/Vision/Audio model": description (attention_k_eq_v shard
+ *        duplication; sliding/global head-dim and kv-head remap; hybrid
+ *        SWA).
  *
  * Semantics (the readings taken where the pages are silent):
  *   - RoPE is rotate-half: pair (k, k + D/2) turns by pos * theta^(-2k/D);
@@ -58,7 +60,7 @@ extern "C" {
 
 #define G4_ABI_VERSION 1
 
-/* Status codes. */
+/* Status codes (library plumbing; no passage of the pages defines them). */
 #define G4_OK 0
 #define G4_ERR_INVALID_ARG (-1) /* null pointer, bad size, bad index            */
 #define G4_ERR_UNSUPPORTED (-2) /* head_dim not 256/512, Hq % Hkv != 0, kind    */
@@ -66,25 +68,48 @@ extern "C" {
 #define G4_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required   */
 #define G4_ERR_HIP (-5)         /* the HIP runtime rejected a launch            */
 
-/* Layer kinds (attention_pattern: 0 = sliding, 1 = full). */
+/* Layer kinds: the attention_pattern values of [FR] Blocker 2 (0 = sliding,
+ * 1 = full; full attention on every fifth layer, indices 4, 9, ..., 34). */
 #define G4_SLIDING 0
 #define G4_FULL 1
 
 /*
  * Per-layer descriptor.  A stack of layers is an array of these; layer
- * indices below refer to positions in that array.
- *   kind            G4_SLIDING or G4_FULL
- *   head_dim        256 or 512 (anything else -> G4_ERR_UNSUPPORTED)
- *   num_q_heads     Hq >= 1
- *   num_kv_heads    Hkv >= 1 with Hq % Hkv == 0
- *   window          sliding: W > 0 keys visible including self; full: 0
- *   kv_alias        1: values are read from the key buffer (raw keys)
+ * indices below refer to positions in that array.  [FR] "What Would Need to
+ * Change" item 3 asks for exactly this per-layer configuration (per-layer
+ * head size, a KV sharing map); [HF] asks for an attention operator that
+ * receives the RoPE and KV-cache parameters directly.
+ *
+ *   kind            G4_SLIDING or G4_FULL -- [FR] Blocker 2 (attention_pattern);
+ *                   [LD] module comment ("Sliding + full attention pattern").
+ *   head_dim        256 or 512 (anything else -> G4_ERR_UNSUPPORTED) --
+ *                   [FR] Blocker 2 (head_dim 256 sliding, global_head_dim 512
+ *                   full) and "What Would Need to Change" item 3.
+ *   num_q_heads     Hq >= 1 -- [SG] description (the sliding/global kv-head
+ *                   remap: head counts differ by layer kind).
+ *   num_kv_heads    Hkv >= 1 with Hq % Hkv == 0 -- [SG] as above; [LD]
+ *                   kv_layer_dims (per-layer KV dimensions).
+ *   window          sliding: W > 0 keys visible including self; full: 0 --
+ *                   [FR] Blocker 2 (sliding attention); [SG] "hybrid SWA".
+ *                   The width convention (W keys including the query's own
+ *                   position) is a reading: the pages give none.
+ *   kv_alias        1: values are read from the key buffer (raw keys) --
+ *                   [LD] supports_tp comment (K=V aliasing in sliding layers,
+ *                   one slice serving K and V); [SG] attention_k_eq_v.
  *   kv_source_layer -1: the layer owns its cache; otherwise the index of an
  *                   EARLIER layer that owns a cache (its own source is -1)
  *                   with equal head_dim, num_kv_heads and kv_alias; the layer
- *                   then reads that layer's buffers
- *   scale           softmax scale; 0 means 1/sqrt(head_dim)
- *   rope_theta      RoPE base (> 0), e.g. 1e4 sliding, 1e6 full
+ *                   then reads that layer's buffers -- [FR] Blocker 3 (35
+ *                   layers, 15 unique KV caches, num_kv_shared_layers 20) and
+ *                   "What Would Need to Change" items 2 (N layers -> M unique
+ *                   caches) and 3 (a KV sharing map).
+ *   scale           softmax scale; 0 means 1/sqrt(head_dim) -- the pages are
+ *                   silent; the scale of scaled dot-product attention
+ *                   ([HF], sdpa_attention_forward) is taken.
+ *   rope_theta      RoPE base (> 0), e.g. 1e4 sliding, 1e6 full -- [FR]
+ *                   "Gemma 4 Model Details" (separate theta values for
+ *                   sliding and full attention); [LD] module comment (dual
+ *                   RoPE theta).
  */
 typedef struct {
   int32_t kind;
@@ -98,41 +123,59 @@ typedef struct {
   double rope_theta;
 } g4_layer_desc;
 
-/* ABI version of the loaded library (G4_ABI_VERSION at build time). */
+/* ABI version of the loaded library (G4_ABI_VERSION at build time).  Library
+ * plumbing; no passage of the pages defines it. */
 int gemma4_abi_version(void);
 
-/* Static name of a status code ("G4_OK", "G4_ERR_WORKSPACE", ...). */
+/* Static name of a status code ("G4_OK", "G4_ERR_WORKSPACE", ...).  Library
+ * plumbing. */
 const char* gemma4_status_string(int status);
 
-/* Detail message of the last failing call on this thread ("" if none). */
+/* Detail message of the last failing call on this thread ("" if none).
+ * Library plumbing. */
 const char* gemma4_last_error(void);
 
 /*
- * Validate a whole stack of descriptors (host only; touches no GPU state).
- * Returns G4_OK or the first error found; every entry point below runs the
- * same checks for the layers it reads.
+ * Validate a whole stack of descriptors (host only; touches no GPU state):
+ * the per-layer head sizes and the KV sharing map of [FR] "What Would Need
+ * to Change" item 3, checked so that every shared layer reads an earlier
+ * owner of matching shape (the shape mismatch of [FR] Blocker 2 becomes an
+ * error code instead of a fault).  Returns G4_OK or the first error found;
+ * every entry point below runs the same checks for the layers it reads.
  */
 int gemma4_validate_layers(const g4_layer_desc* layers, int32_t n_layers);
 
 /*
  * Cache bytes a layer owns for a batch of `batch` sequences of capacity
- * `max_len`: k = batch*Hkv*max_len*head_dim*2 (bf16), v = the same unless the
- * layer is aliased (v = 0).  A shared layer owns nothing (both 0).
+ * `max_len` -- [FR] "What Would Need to Change" item 2 (variable-size KV
+ * cache buffers per layer; N layers -> M unique caches):
+ * k = batch*Hkv*max_len*head_dim*2 (bf16, layout [batch, Hkv, max_len,
+ * head_dim] of raw keys), v = the same unless the layer is aliased (v = 0,
+ * [LD] supports_tp).  A shared layer owns nothing (both 0).  Host only.
  */
 int gemma4_kv_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch, int32_t max_len,
                     size_t* k_bytes, size_t* v_bytes);
 
-/* Device workspace bytes gemma4_attn_prefill needs for this layer and shape. */
+/* Device workspace bytes gemma4_attn_prefill needs for this layer and shape
+ * (rotated key and value operand tiles, arrival counters, partial results of
+ * query tiles split across work-groups).  Host only.  The operation it
+ * serves is cited at gemma4_attn_prefill. */
 int gemma4_prefill_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch,
                                    int32_t seq_len, size_t* bytes);
 
-/* Device workspace bytes gemma4_attn_decode needs; max_kv_len bounds kv_len[]. */
+/* Device workspace bytes gemma4_attn_decode needs (split-K partial outputs
+ * and log-sum-exps); max_kv_len bounds kv_len[].  Host only.  The operation
+ * it serves is cited at gemma4_attn_decode. */
 int gemma4_decode_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch,
                                   int32_t max_kv_len, size_t* bytes);
 
 /*
  * Prefill: queries at positions 0..seq_len-1 attend to cache rows
- * 0..seq_len-1 of the layer's (or its source layer's) cache.
+ * 0..seq_len-1 of the layer's (or its source layer's) cache.  The attention
+ * operator of [HF] (sdpa_attention_forward intercepted so that the operator
+ * receives positional dual-RoPE and KV-cache parameters), for the
+ * per-layer head sizes of [FR] Blocker 2 and the shared caches of [FR]
+ * Blocker 3.
  *   q          bf16 [batch, seq_len, Hq, head_dim], raw (pre-RoPE)
  *   k_cache    host array of n_layers device pointers; entry src(layer) is
  *              bf16 [batch, Hkv, max_len, head_dim] of raw keys whose rows
@@ -151,7 +194,9 @@ int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t l
 /*
  * Decode: one query per sequence at position kv_len[b]-1 attends to cache
  * rows 0..kv_len[b]-1 (only the last `window` of them for a sliding layer).
- * The current token's key/value must already be in the cache.
+ * The current token's key/value must already be in the cache.  The same
+ * attention operator as prefill ([HF]), reading the per-layer KV caches of
+ * [FR] "What Would Need to Change" item 2.
  *   q          bf16 [batch, Hq, head_dim], raw (pre-RoPE)
  *   k_cache    as for prefill; rows >= kv_len[b] are never read
  *   v_cache    as for prefill
@@ -163,6 +208,7 @@ int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t l
  *              device, so it needs no host copy of the lengths)
  *   out        fp32 [batch, Hq, head_dim]
  *   workspace  device scratch of at least gemma4_decode_workspace_bytes()
+ * Requires Hq / Hkv <= 16.
  */
 int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
                        void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
@@ -170,12 +216,13 @@ int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t la
                        void* stream);
 
 /*
- * Profiling aid (not part of the attention computation).  After this call,
- * each compute call made on the calling thread records `before` on its
- * stream immediately before launching its main attention kernel (prefill:
- * the kernel after the key-rotation pass; decode: the split-K kernel before
- * the merge) and `after` immediately after it.  The events are caller-owned
- * hipEvent_t handles passed as void*; NULL, NULL turns recording off.
+ * Profiling aid (not part of the attention computation; no passage of the
+ * pages defines it).  After this call, each compute call made on the
+ * calling thread records `before` on its stream immediately before
+ * launching its main attention kernel (prefill: the kernel after the
+ * key-rotation pass; decode: the split-K kernel before the merge) and
+ * `after` immediately after it.  The events are caller-owned hipEvent_t
+ * handles passed as void*; NULL, NULL turns recording off.
  * Returns G4_OK, or G4_ERR_INVALID_ARG if exactly one of the two is NULL.
  */
 int gemma4_set_profile_events(void* before, void* after);

@@ -70,12 +70,28 @@ def _load():
         lib.orc_attention_row.argtypes = [_u16p, _u16p, _u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int32, ctypes.c_double, ctypes.c_double, _f64p, _f64p]
         lib.orc_attention_row.restype = ctypes.c_int
+        lib.orc_scores_row.argtypes = [_u16p, _u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_double, ctypes.c_double, _f64p]
+        lib.orc_scores_row.restype = ctypes.c_int
         lib.orc_prefill.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_double, ctypes.c_double, _u16p, _u16p, _u16p,
                                                            _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
         lib.orc_prefill.restype = ctypes.c_int
         lib.orc_decode.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_double, ctypes.c_double, _u16p, _u16p, _u16p,
                                                           _i32p, _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
         lib.orc_decode.restype = ctypes.c_int
+        vp = ctypes.c_void_p
+        lib.orc_prefill_ext.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_double, ctypes.c_double, _u16p, vp, vp,
+                                                               ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                                               ctypes.c_int32, _i32p, _i64p, ctypes.c_int64, _f64p,
+                                                               ctypes.c_int32]
+        lib.orc_prefill_ext.restype = ctypes.c_int
+        lib.orc_decode_ext.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_double, ctypes.c_double, _u16p, vp, vp,
+                                                              ctypes.c_int32, ctypes.c_double, ctypes.c_double, _i32p,
+                                                              ctypes.c_int64, _i64p, ctypes.c_int64, _f64p,
+                                                              ctypes.c_int32]
+        lib.orc_decode_ext.restype = ctypes.c_int
+        lib.orc_fp8_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.orc_fp8_e4m3_to_f64.restype = ctypes.c_double
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -132,18 +148,70 @@ def attention_row(q: np.ndarray, k_slice: np.ndarray, v_slice: Optional[np.ndarr
     return w, o
 
 
+def scores_row(q: np.ndarray, k_slice: np.ndarray, pos: int, length: int, window: int, theta: float,
+               scale: float = 0.0) -> np.ndarray:
+    """Scores (natural units) of one query row over one (batch, kv-head) cache slice.
+
+    Returns ``length`` doubles: scale * <RoPE(q, pos), RoPE(k_j, j)> for the
+    keys visible from ``pos``, -inf for the others.
+    """
+    q = _u16(q)
+    k_slice = _u16(k_slice)
+    D = q.shape[-1]
+    s = np.empty(length, np.float64)
+    rc = _load().orc_scores_row(_ptr(q, _u16p), _ptr(k_slice, _u16p), D, pos, length, window, theta, scale,
+                                _ptr(s, _f64p))
+    if rc != 0:
+        raise ValueError("oracle: invalid scores row")
+    return s
+
+
+KV_BF16, KV_FP8 = 0, 1
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Exact values of OCP E4M3 bytes (NaN for the two NaN codes)."""
+    lib = _load()
+    c = np.asarray(codes, np.uint8)
+    return np.array([lib.orc_fp8_e4m3_to_f64(int(x)) for x in c.ravel()], np.float64).reshape(c.shape)
+
+
+def _kv(a: Optional[np.ndarray]):
+    """A cache tensor: uint16 (bf16 bits) or uint8 (E4M3 bytes); returns (array, format)."""
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a, KV_BF16
+    if a.dtype == np.uint8:
+        return a, KV_FP8
+    raise TypeError("cache tensors are uint16 (bfloat16 bits) or uint8 (E4M3 bytes)")
+
+
+def _vptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
 def prefill(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], window: int, theta: float, scale: float = 0.0,
-            rows: Optional[Sequence[int]] = None, nthreads: int = 0) -> np.ndarray:
-    """Prefill attention; q [B,S,Hq,D], k/v [B,Hkv,Lmax,D] (v None = aliased).
+            rows: Optional[Sequence[int]] = None, nthreads: int = 0, start_pos: int = 0,
+            span_end: Optional[np.ndarray] = None, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Prefill attention; q [B,S,Hq,D] at positions start_pos..start_pos+S-1,
+    k/v [B,Hkv,Lmax,D] (bf16 bits, or E4M3 bytes times k_scale / v_scale;
+    v None = aliased), span_end None (causal) or int32 [B,S] (last position
+    of each query's bidirectional span).
 
     Returns fp64 [B,S,Hq,D], or [len(rows), D] for flattened rows b*S*Hq+s*Hq+h.
     """
-    q, k = _u16(q), _u16(k)
-    v = None if v is None else _u16(v)
+    q = _u16(q)
+    k, kf = _kv(k)
+    v, vf = _kv(v)
     B, S, Hq, D = q.shape
     _, Hkv, Lmax, Dk = k.shape
-    if Dk != D or (v is not None and v.shape != k.shape):
+    if Dk != D or (v is not None and (v.shape != k.shape or vf != kf)):
         raise ValueError("shape mismatch")
+    se = None if span_end is None else np.ascontiguousarray(span_end, dtype=np.int32)
+    if se is not None and se.shape != (B, S):
+        raise ValueError("span_end must be [B, S]")
     if rows is None:
         out = np.empty((B, S, Hq, D), np.float64)
         r, n = None, -1
@@ -151,32 +219,43 @@ def prefill(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], window: int, 
         r = np.ascontiguousarray(rows, dtype=np.int64)
         n = r.shape[0]
         out = np.empty((n, D), np.float64)
-    rc = _load().orc_prefill(B, S, Hq, Hkv, D, Lmax, window, theta, scale, _ptr(q, _u16p), _ptr(k, _u16p),
-                            _ptr(v, _u16p), _ptr(r, _i64p), n, _ptr(out, _f64p), nthreads)
+    rc = _load().orc_prefill_ext(B, S, Hq, Hkv, D, Lmax, window, theta, scale, _ptr(q, _u16p), _vptr(k), _vptr(v),
+                                 kf, k_scale, v_scale, start_pos, _ptr(se, _i32p), _ptr(r, _i64p), n,
+                                 _ptr(out, _f64p), nthreads)
     if rc != 0:
         raise ValueError("oracle: invalid prefill arguments")
     return out
 
 
 def decode(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], kv_len: np.ndarray, window: int, theta: float,
-           scale: float = 0.0, rows: Optional[Sequence[int]] = None, nthreads: int = 0) -> np.ndarray:
-    """Decode attention; q [B,Hq,D], k/v [B,Hkv,Lmax,D], kv_len [B] (host)."""
-    q, k = _u16(q), _u16(k)
-    v = None if v is None else _u16(v)
-    B, Hq, D = q.shape
+           scale: float = 0.0, rows: Optional[Sequence[int]] = None, nthreads: int = 0, ring: int = 0,
+           k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Decode attention; q [B,Hq,D] (one token at kv_len-1) or [B,T,Hq,D] (T
+    tokens at kv_len-T .. kv_len-1), k/v [B,Hkv,Lmax,D] (bf16 bits or E4M3
+    bytes; with ring = Lmax > 0, position j in row j % ring), kv_len [B] (host).
+    Returns fp64 shaped like q, or [len(rows), D]."""
+    q = _u16(q)
+    multi = q.ndim == 4
+    if multi:
+        B, T, Hq, D = q.shape
+    else:
+        (B, Hq, D), T = q.shape, 1
+    k, kf = _kv(k)
+    v, vf = _kv(v)
     _, Hkv, Lmax, Dk = k.shape
-    if Dk != D or (v is not None and v.shape != k.shape):
+    if Dk != D or (v is not None and (v.shape != k.shape or vf != kf)):
         raise ValueError("shape mismatch")
     kl = np.ascontiguousarray(kv_len, dtype=np.int32)
     if rows is None:
-        out = np.empty((B, Hq, D), np.float64)
+        out = np.empty(q.shape, np.float64)
         r, n = None, -1
     else:
         r = np.ascontiguousarray(rows, dtype=np.int64)
         n = r.shape[0]
         out = np.empty((n, D), np.float64)
-    rc = _load().orc_decode(B, Hq, Hkv, D, Lmax, window, theta, scale, _ptr(q, _u16p), _ptr(k, _u16p),
-                            _ptr(v, _u16p), _ptr(kl, _i32p), _ptr(r, _i64p), n, _ptr(out, _f64p), nthreads)
+    rc = _load().orc_decode_ext(B, T, Hq, Hkv, D, Lmax, window, theta, scale, _ptr(q, _u16p), _vptr(k), _vptr(v), kf,
+                                k_scale, v_scale, _ptr(kl, _i32p), ring, _ptr(r, _i64p), n, _ptr(out, _f64p),
+                                nthreads)
     if rc != 0:
         raise ValueError("oracle: invalid decode arguments")
     return out

@@ -11,9 +11,14 @@ if ROOT not in sys.path:
 from hybrid_sliding_global_amd import inputs  # noqa: E402
 
 # Tolerance fixed by the method's bf16-input / fp32-accumulate arithmetic:
-# max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3.
+# max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3.  Long rows
+# average many value rows, so their outputs are small (RMS ~ 1/sqrt(keys))
+# and the absolute bounds loosen relative to them; the relative RMS error
+# (about 1e-3 observed: bf16 rounding of the rotated operands and of P) is
+# gated at 1e-2 as well, which a dropped or doubled key tile exceeds.
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
+REL_RMS = 1e-2
 
 
 def to_dev(a: np.ndarray):
@@ -22,7 +27,7 @@ def to_dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 
-def check(got, want, tag: str, max_abs: float = MAX_ABS, mean_abs: float = MEAN_ABS):
+def check(got, want, tag: str, max_abs: float = MAX_ABS, mean_abs: float = MEAN_ABS, rel_rms: float = REL_RMS):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (tag, got.shape, want.shape)
@@ -31,7 +36,8 @@ def check(got, want, tag: str, max_abs: float = MAX_ABS, mean_abs: float = MEAN_
     mx, mn = float(err.max()), float(err.mean())
     rel = float(np.sqrt((err ** 2).mean() / max((want ** 2).mean(), 1e-30)))
     print("%s: max_abs %.3e mean_abs %.3e rel_rms %.3e" % (tag, mx, mn, rel), flush=True)
-    assert mx <= max_abs and mn <= mean_abs, "%s: max_abs %.3e mean_abs %.3e" % (tag, mx, mn)
+    assert mx <= max_abs and mn <= mean_abs and rel <= rel_rms, \
+        "%s: max_abs %.3e mean_abs %.3e rel_rms %.3e" % (tag, mx, mn, rel)
     return mx, mn
 
 

@@ -39,6 +39,34 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, n), n
 
 
+CITE_TAGS = ("[FR]", "[HF]", "[LD]", "[SG]")
+UNCITED_OK = ("no passage of the pages defines", "Library plumbing", "is cited at")
+
+
+def _decl_comments():
+    """(declaration, the comment block right above it) for every function the header declares."""
+    text = open(HEADER).read()
+    out = []
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*\n((?:[^;/])*?\b(gemma4_\w+)\s*\([^;]*;)", text, flags=re.S):
+        out.append((m.group(3), re.sub(r"\s*\n\s*\*\s*", " ", m.group(1))))
+    return out
+
+
+def test_every_header_declaration_cites_its_passage():
+    decls = dict(_decl_comments())
+    assert set(decls) == set(header_functions())
+    for name, comment in decls.items():
+        assert any(t in comment for t in CITE_TAGS + UNCITED_OK), "%s has no citation" % name
+    # every descriptor field names the passage that defines it
+    text = open(HEADER).read()
+    block = text[text.index("Per-layer descriptor."):text.index("typedef struct")]
+    for field in ("kind", "head_dim", "num_q_heads", "num_kv_heads", "window", "kv_alias", "kv_source_layer",
+                  "scale", "rope_theta"):
+        m = re.search(r"\n \*   %s\s+(.*?)(?=\n \*   \w+\s{2,}|\n \*/)" % field, block, flags=re.S)
+        assert m, field
+        assert any(t in m.group(1) for t in CITE_TAGS), "field %s has no citation" % field
+
+
 def test_abi_version_and_status_strings(lib):
     assert L.abi_version() == 1
     for code, name in [(0, "G4_OK"), (-1, "G4_ERR_INVALID_ARG"), (-2, "G4_ERR_UNSUPPORTED"),
@@ -110,77 +138,57 @@ def test_kv_bytes_and_sharing(lib):
     assert total_k + total_v == 12 * 2048 * 256 * 2 + 3 * 2 * (2 * 2048 * 512 * 2) == 37748736
 
 
-def _prefill_ws_model(B, S, Hq, Hkv, D, W, rows_forced=None):
-    """Workspace layout of a prefill call: key and value operand images,
-    arrival counters, partial-result slots of the query tiles split across
-    work-groups.  The work split is chosen by the same cost model as the
-    library (per-tile, per-segment and per-split cycle costs; head size 256
-    also considers 64-row query tiles, which are never split).  Returns
-    (bytes, pieces, rows)."""
-    import math
-    BN = 32
-    ntiles = -(-S // BN)
-    g = Hq // Hkv
-    best = None
-    for rows in (128, 64):
-        if rows == 64 and D != 256:
-            continue
-        if rows_forced and rows != rows_forced:
-            continue
-        nqt = -(-(S * g) // rows)
+def _ws_parts(B, S, Hq, Hkv, D, rows):
+    """Lower bounds of the prefill workspace: both operand images (rotated
+    keys and values, 32-key tiles, bf16) and one arrival counter per query
+    tile of ``rows`` rows, each part rounded up to 256 bytes; and the size of
+    one partial-result slot (a 32 x D fp32 block per row group plus the
+    running maximum and sum of every lane)."""
+    rnd = lambda x: -(-x // 256) * 256  # noqa: E731
+    img = rnd(B * Hkv * (-(-S // 32)) * 32 * D * 2)
+    nqt = -(-(S * (Hq // Hkv)) // rows)
+    base = rnd(2 * img + B * Hkv * nqt * 4)
+    waves = 8 if D == 512 else 4
+    return base, 32 * D * 16 + waves * 64 * 2 * 4
 
-        def keys(qt):
-            r0 = qt * rows
-            pmin, pmax = r0 // g, min(r0 + rows - 1, S * g - 1) // g
-            return (max(0, pmin - W + 1) if W > 0 else 0) // BN, pmax // BN
 
-        if D == 512:
-            tile, segment, split = 4700.0, 12000.0, 40000.0
-        elif rows == 64:
-            tile, segment, split = 1400.0, 12000.0, 0.0
-        else:
-            tile, segment, split = 2400.0, 15000.0, 30000.0
-        for paired in (1, 0):
-            nunits = (nqt + 1) // 2 if paired else nqt
-            umax = 1
-            for i in range(nunits):
-                if paired:
-                    a0, a1 = keys(nqt - 1 - i)
-                    b0, b1 = keys(i) if i < nqt - 1 - i else (0, -1)
-                else:
-                    (a0, a1), (b0, b1) = keys(i), (0, -1)
-                umax = max(umax, (a1 - a0 + 1) + (b1 - b0 + 1))
-            groups = B * Hkv * nunits
-            kmax = 1 if rows == 64 else max(1, min(256 // groups, umax, 64))
-            for k in range(1, kmax + 1):
-                rounds = math.ceil(groups * k / 256)
-                segs = (2.0 if k <= 2 else 1.5) if paired else 1.0
-                t = rounds * (math.ceil(umax / k) * tile + segs * segment + (split if k > 1 else 0.0))
-                if best is None or t < best[0]:
-                    best = (t, groups, k, rows, nqt)
-    _, groups, k, rows, nqt = best
-    img = -(-(B * Hkv * ntiles * BN * D * 2) // 256) * 256
-    cnt = 2 * img
-    part = -(-(cnt + B * Hkv * nqt * 4) // 256) * 256
-    nw = 8 if D == 512 else 4  # waves per work-group
-    slot = 32 * D * 16 + nw * 64 * 2 * 4
-    return part + (groups * k * 2 * slot if k > 1 else 0), k, rows
+def _split_slots(B, S, Hq, Hkv, D, W):
+    """Number of partial-result slots the workspace holds beyond images and
+    counters, for whichever query-tile height the library picked (None if no
+    height explains the size)."""
+    stack = [wl.layer_desc(wl.SLIDING if W else wl.FULL, D, Hq, Hkv, 1e4, W, 0)]
+    ws = L.prefill_workspace_bytes(stack, 0, B, S)
+    for rows in ((128, 64) if D == 256 else (128,)):
+        base, slot = _ws_parts(B, S, Hq, Hkv, D, rows)
+        if ws >= base and (ws - base) % slot == 0:
+            return (ws - base) // slot
+    return None
 
 
 def test_workspace_sizes(lib):
+    """Properties of the prefill workspace size: it holds the operand images
+    and counters, plus whole partial-result slots only when query tiles are
+    cut into pieces (two slots per work-group, each work-group covering up to
+    two query tiles)."""
+    # one key tile: nothing can be split, so there are no slots
+    for D, W in ((512, 0), (256, 0), (256, 16)):
+        for S in (1, 17, 32):
+            assert _split_slots(1, S, 8, 2, D, W) == 0
+    # the 4096-token full layer is cut into pieces: slots present
+    n = _split_slots(1, 4096, 8, 2, 512, 0)
+    assert n is not None and n > 0 and n % 2 == 0
+    # windowed 2048-token sliding layer (128 query tiles of 128 rows): whole tiles per work-group
+    assert _split_slots(1, 2048, 8, 1, 256, 512) == 0
+    # every shape is explained by images + counters + whole slots
+    for (B, S, Hq, Hkv, D, W) in ((2, 333, 8, 1, 256, 48), (1, 1024, 8, 1, 256, 0), (1, 640, 8, 2, 512, 0),
+                                  (3, 257, 16, 2, 256, 100), (1, 2048, 8, 2, 512, 0)):
+        assert _split_slots(B, S, Hq, Hkv, D, W) is not None, (B, S, Hq, Hkv, D, W)
     stack = wl.gemma4_stack()
-    for layer in (0, 4):
-        d = stack[layer]
-        for S in (1, 100, 2048, 4096):
-            want = _prefill_ws_model(1, S, d["num_q_heads"], d["num_kv_heads"], d["head_dim"], d["window"])[0]
-            assert L.prefill_workspace_bytes(stack, layer, 1, S) == want
-    # the 4096-token full layer is cut into two pieces per pair of query tiles
-    assert _prefill_ws_model(1, 4096, 8, 2, 512, 0)[1] == 2
-    # the stack's sliding layers (128 tiles of 128 rows) run 64-row tiles
-    assert _prefill_ws_model(1, 2048, 8, 1, 256, 512)[2] == 64
-    assert L.prefill_workspace_bytes(stack, 0, 1, 2048) >= 1 * 1 * 2048 * 256 * 2
+    assert L.prefill_workspace_bytes(stack, 0, 1, 2048) >= 2 * 1 * 1 * 2048 * 256 * 2
     w = L.decode_workspace_bytes(stack, 4, 64, 8192)
-    assert w > 0 and w % 4 == 0
+    # one fp32 partial (head_dim values and a log-sum-exp) per query head for
+    # every stream plus every piece of the split: (B*Hkv + 512) * g * (D + 1) * 4
+    assert w == (64 * 2 + 512) * 4 * (512 + 1) * 4
     with pytest.raises(L.Gemma4Error):
         L.prefill_workspace_bytes(stack, 4, 0, 2048)
 

@@ -16,19 +16,27 @@ MUTATIONS = {
     "rope_exponent": ("out[k] = pow(theta, -2.0", "out[k] = pow(theta, -1.0", None),
     "rope_interleaved_pairs": ("double x0 = x[k], x1 = x[k + half];",
                                "double x0 = x[2 * k % D], x1 = x[(2 * k + 1) % D];", None),
-    "key_position": ("orc_rope_row_bf16(kbase + (size_t)j * D, D, f, (double)j, tmp, krot + (size_t)j * D);\n    free",
-                     "orc_rope_row_bf16(kbase + (size_t)j * D, D, f, (double)(j + 1), tmp, krot + (size_t)j * D);\n    free",
+    "key_position": ("orc_rope_freq(tmp, D, f, (double)j, krot + (size_t)j * D);\n    }\n    free(tmp);",
+                     "orc_rope_freq(tmp, D, f, (double)(j + 1), krot + (size_t)j * D);\n    }\n    free(tmp);",
                      None),
     "window_off_by_one": ("if (W > 0 && p - j >= W) return 0;", "if (W > 0 && p - j > W) return 0;", None),
-    "causal_off_by_one": ("if (j < 0 || j > p || j >= L) return 0;", "if (j < 0 || j > p + 1 || j >= L) return 0;",
+    "causal_off_by_one": ("if (j < 0 || j > e || j >= L) return 0;", "if (j < 0 || j > e + 1 || j >= L) return 0;",
                           None),
     "scale": ("scale = 1.0 / sqrt((double)D);", "scale = 1.0 / (double)D;", None),
     "gqa_prefill_map": ("if (rb != b || h / g != kvh) continue;", "if (rb != b || h % Hkv != kvh) continue;", 0),
     "gqa_decode_map": ("if (rb != b || h / g != kvh) continue;", "if (rb != b || h % Hkv != kvh) continue;", 1),
-    "decode_position": ("qpos[nq] = L - 1;", "qpos[nq] = L;", None),
-    "value_row_index": ("const uint16_t* v = vbase + (size_t)j * (size_t)D;",
-                         "const uint16_t* v = vbase + (size_t)(j / 2) * (size_t)D;",
-                         None),
+    "decode_position": ("qpos[nq] = L - T + t;", "qpos[nq] = L - T + t + 1;", None),
+    "value_row_index": ("orc_row(vr, j, D, v);", "orc_row(vr, j / 2, D, v);", None),
+    "values_from_rotated_keys": ("for (int32_t d = 0; d < D; ++d) out[d] += w * v[d];",
+                                 "for (int32_t d = 0; d < D; ++d) out[d] += w * krot[(size_t)j * D + d];", None),
+    "fp8_exponent_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);", None),
+    "fp8_subnormal_scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);", None),
+    "fp8_alias_value_scale": ("const double vs = v ? v_scale : k_scale;", "const double vs = v_scale;", None),
+    "ring_row": ("const int64_t r = c->ring > 0 ? j % c->ring : j;",
+                 "const int64_t r = c->ring > 0 ? (j + 1) % c->ring : j;", None),
+    "chunk_query_position": ("qpos[nq] = start_pos + s;", "qpos[nq] = s;", None),
+    "span_ignored": ("if (j < 0 || j > e || j >= L) return 0;", "if (j < 0 || j > p || j >= L) return 0;", None),
+    "verify_all_at_last_position": ("qpos[nq] = L - T + t;", "qpos[nq] = L - 1;", None),
     "softmax_no_max_shift": ("s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);",
                              "s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m) + 1e-3;", None),
 }

@@ -257,6 +257,36 @@ def test_row_subset_matches_full(orc):
     assert np.array_equal(sub, full.reshape(-1, 32)[rows])
 
 
+# ------------------------------------------------------------ scores ------
+
+def _rot_complex(x, pos, theta):
+    """Rotate-half RoPE in its complex form: z_k = x_k + i x_{k+D/2} times exp(i pos theta^(-2k/D))."""
+    D = x.shape[-1]
+    h = D // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    freq = np.exp(-np.arange(h) * (2.0 / D) * np.log(theta))
+    zr = z * np.exp(1j * np.asarray(pos, np.float64)[..., None] * freq)
+    return np.concatenate([zr.real, zr.imag], axis=-1)
+
+
+@pytest.mark.parametrize("D,theta,W,p", [(256, 1e4, 0, 39), (512, 1e6, 7, 30), (16, 1e4, 3, 0)])
+def test_scores_match_independent_rotation(orc, D, theta, W, p):
+    L = 40
+    q = bf16((D,), [915, D, 0])
+    k = bf16((L, D), [915, D, 1])
+    got = orc.scores_row(q, k, p, L, W, theta)
+    kr = _rot_complex(widen(k), np.arange(L), theta)
+    qr = _rot_complex(widen(q), p, theta)
+    want = kr @ qr / math.sqrt(D)
+    vis = np.array([j <= p and (W == 0 or p - j < W) for j in range(L)])
+    assert np.all(np.isneginf(got[~vis]))
+    assert np.max(np.abs(got[vis] - want[vis])) < 1e-10
+    # the weights are the softmax of these scores
+    w, _ = orc.attention_row(q, k, None, p, L, W, theta)
+    e = np.exp(got[vis] - got[vis].max())
+    assert np.max(np.abs(w[vis] - e / e.sum())) < 1e-12
+
+
 # ------------------------------------------------ library cross-check ------
 
 def _sdpa_reference(q, k, v, W, theta, kv_len=None):
@@ -344,3 +374,221 @@ def test_generator_is_deterministic():
     assert inputs.sha256(a) == inputs.sha256(b) != inputs.sha256(c)
     f = inputs.f32_from_bf16_bits(inputs.normal_bf16([2, 0, 0], (1 << 16,)))
     assert abs(f.mean()) < 0.02 and abs(f.std() - 1.0) < 0.02
+
+
+# ------------------------------------------- next rows: E4M3 KV elements ---
+
+def test_fp8_e4m3_decoding_matches_torch(orc):
+    """Every one of the 256 E4M3 codes against torch's float8_e4m3fn (OCP)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.fp8_e4m3_value(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], want[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0 and got[0xB8] == -1.0
+
+
+def _fp8_cache(shape, seed):
+    """E4M3 codes of N(0,1) samples (torch's round-to-nearest conversion)."""
+    import torch
+    x = torch.from_numpy(np.random.default_rng(seed).standard_normal(shape).astype(np.float32))
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _bf16_of(values):
+    return inputs.bf16_bits_from_f32(values.astype(np.float32))
+
+
+@pytest.mark.parametrize("alias", [False, True])
+def test_fp8_cache_equals_bf16_cache_of_its_values(orc, alias):
+    """An E4M3 cache with power-of-two scales holds values bf16 represents
+    exactly, so attention over it equals attention over that bf16 cache, bit
+    for bit (prefill and decode)."""
+    B, S, Hq, Hkv, D = 2, 21, 4, 2, 32
+    ks, vs = 0.125, 4.0
+    k8 = _fp8_cache((B, Hkv, S, D), [920, 1])
+    v8 = None if alias else _fp8_cache((B, Hkv, S, D), [920, 2])
+    kb = _bf16_of(orc.fp8_e4m3_value(k8) * ks)
+    vb = None if alias else _bf16_of(orc.fp8_e4m3_value(v8) * vs)
+    assert np.array_equal(inputs.f32_from_bf16_bits(kb), (orc.fp8_e4m3_value(k8) * ks).astype(np.float32))
+    q = bf16((B, S, Hq, D), [920, 0])
+    got = orc.prefill(q, k8, v8, 6, 1e4, k_scale=ks, v_scale=vs)
+    assert np.array_equal(got, orc.prefill(q, kb, vb, 6, 1e4))
+    qd = bf16((B, Hq, D), [920, 3])
+    kv = np.array([S, 7], np.int32)
+    got = orc.decode(qd, k8, v8, kv, 0, 1e6, k_scale=ks, v_scale=vs)
+    assert np.array_equal(got, orc.decode(qd, kb, vb, kv, 0, 1e6))
+
+
+def test_fp8_decode_matches_torch_sdpa(orc):
+    """E4M3 cache dequantised by torch's own float8 conversion, then torch SDPA."""
+    import torch
+    B, Hq, Hkv, D, Lmax = 2, 4, 2, 64, 30
+    ks, vs = 0.75, 1.5
+    k8 = _fp8_cache((B, Hkv, Lmax, D), [921, 1])
+    v8 = _fp8_cache((B, Hkv, Lmax, D), [921, 2])
+    q = bf16((B, Hq, D), [921, 0])
+    kv = np.array([30, 11], np.int32)
+    got = orc.decode(q, k8, v8, kv, 9, 1e4, k_scale=ks, v_scale=vs)
+    deq = lambda a, s: torch.from_numpy(a).view(torch.float8_e4m3fn).to(torch.float64).numpy() * s  # noqa: E731
+    want = _sdpa_reference_values(q, deq(k8, ks), deq(v8, vs), 9, 1e4, kv)
+    assert np.max(np.abs(got - want)) < 1e-10
+
+
+def _sdpa_reference_values(q, kf, vf, W, theta, kv_len):
+    """torch SDPA (float64) for decode queries [B, Hq, D] over fp64 key/value
+    caches [B, Hkv, Lmax, D] (keys rotated here by the complex form)."""
+    import torch
+    B, Hkv, Lmax, D = kf.shape
+    Hq = q.shape[1]
+    kr = _rot_complex(kf, np.arange(Lmax)[None, None, :], theta)
+    lens = np.asarray(kv_len)
+    qr = _rot_complex(widen(q)[:, :, None, :], np.broadcast_to((lens - 1)[:, None, None], (B, Hq, 1)), theta)
+    g = Hq // Hkv
+    mask = np.zeros((B, 1, 1, Lmax), bool)
+    for b in range(B):
+        p = lens[b] - 1
+        for j in range(Lmax):
+            mask[b, 0, 0, j] = j <= p and (W == 0 or p - j < W)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.ascontiguousarray(qr)), torch.from_numpy(np.repeat(kr, g, axis=1).copy()),
+        torch.from_numpy(np.repeat(vf, g, axis=1).copy()), attn_mask=torch.from_numpy(mask))
+    return out.numpy()[:, :, 0, :]
+
+
+# --------------------------------------------- next rows: ring-buffer cache --
+
+@pytest.mark.parametrize("W,C,T", [(8, 8, 1), (8, 11, 1), (5, 9, 3)])
+def test_ring_cache_equals_linear_cache(orc, W, C, T):
+    """A window-sized cache keeping position j in row j % C gives the decode
+    result of the full linear cache, bit for bit; rows holding positions
+    older than every window may hold anything."""
+    B, Hq, Hkv, D, L = 3, 4, 1, 32, 40
+    kl = bf16((B, Hkv, L, D), [922, C, 1])
+    vl = bf16((B, Hkv, L, D), [922, C, 2])
+    q = bf16((B, T, Hq, D), [922, C, 0]) if T > 1 else bf16((B, Hq, D), [922, C, 0])
+    kv = np.array([40, 13, T], np.int32)
+    want = orc.decode(q, kl, vl, kv, W, 1e4)
+    kr = np.full((B, Hkv, C, D), inputs.NAN_BF16, np.uint16)
+    vr = kr.copy()
+    for b in range(B):
+        lo = max(0, kv[b] - T + 1 - W)
+        for j in range(lo, kv[b]):
+            kr[b, :, j % C] = kl[b, :, j]
+            vr[b, :, j % C] = vl[b, :, j]
+    assert np.array_equal(orc.decode(q, kr, vr, kv, W, 1e4, ring=C), want)
+    if C > W + T - 1:  # a ring with spare rows: other layers' positions leave the result alone
+        assert np.isfinite(want).all()
+    with pytest.raises(ValueError):  # a window the ring cannot hold
+        orc.decode(q, kr, vr, kv, C + 1, 1e4, ring=C)
+
+
+# ------------------------------------- next rows: queries against a cache --
+
+@pytest.mark.parametrize("W,alias", [(0, False), (7, True)])
+def test_chunked_prefill_equals_full_prefill(orc, W, alias):
+    """Prefill of positions P0..P0+S-1 over a cache holding 0..P0+S-1 gives the
+    matching rows of the whole prompt's prefill, bit for bit, for any cut."""
+    B, S, Hq, Hkv, D = 2, 37, 4, 2, 32
+    q = bf16((B, S, Hq, D), [923, W, 0])
+    k = bf16((B, Hkv, S + 5, D), [923, W, 1])
+    v = None if alias else bf16((B, Hkv, S + 5, D), [923, W, 2])
+    full = orc.prefill(q, k, v, W, 1e4)
+    for cuts in ([0, 37], [0, 1, 37], [0, 16, 17, 30, 37]):
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            part = orc.prefill(np.ascontiguousarray(q[:, a:b]), k, v, W, 1e4, start_pos=a)
+            assert np.array_equal(part, full[:, a:b])
+
+
+def test_chunked_prefill_matches_torch_sdpa(orc):
+    """Offset positions against torch SDPA on independently rotated vectors."""
+    import torch
+    B, S, P0, Hq, Hkv, D, W, theta = 1, 9, 14, 4, 2, 64, 10, 1e6
+    q = bf16((B, S, Hq, D), [924, 0])
+    k = bf16((B, Hkv, P0 + S, D), [924, 1])
+    v = bf16((B, Hkv, P0 + S, D), [924, 2])
+    got = orc.prefill(q, k, v, W, theta, start_pos=P0)
+    L = P0 + S
+    kr = _rot_complex(widen(k), np.arange(L)[None, None, :], theta)
+    qr = _rot_complex(widen(q).transpose(0, 2, 1, 3), (P0 + np.arange(S))[None, None, :], theta)
+    mask = np.array([[j <= P0 + i and P0 + i - j < W for j in range(L)] for i in range(S)])
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.ascontiguousarray(qr)), torch.from_numpy(np.repeat(kr, Hq // Hkv, axis=1).copy()),
+        torch.from_numpy(np.repeat(widen(v), Hq // Hkv, axis=1).copy()), attn_mask=torch.from_numpy(mask))
+    assert np.max(np.abs(got - out.numpy().transpose(0, 2, 1, 3))) < 1e-10
+
+
+@pytest.mark.parametrize("W", [0, 6])
+def test_multi_token_decode_equals_single_decodes(orc, W):
+    """The T queries of a verify step over a frozen cache: query t equals a
+    one-token decode with kv_len - T + t + 1 keys, and the prefill chunk at
+    kv_len - T, bit for bit."""
+    B, T, Hq, Hkv, D, Lmax = 3, 4, 8, 2, 32, 30
+    q = bf16((B, T, Hq, D), [925, W, 0])
+    k = bf16((B, Hkv, Lmax, D), [925, W, 1])
+    v = bf16((B, Hkv, Lmax, D), [925, W, 2])
+    kv = np.array([30, 4, 17], np.int32)
+    got = orc.decode(q, k, v, kv, W, 1e4)
+    for t in range(T):
+        one = orc.decode(np.ascontiguousarray(q[:, t]), k, v, kv - T + t + 1, W, 1e4)
+        assert np.array_equal(got[:, t], one)
+    for b in range(B):
+        chunk = orc.prefill(np.ascontiguousarray(q[b:b + 1]), np.ascontiguousarray(k[b:b + 1]),
+                            np.ascontiguousarray(v[b:b + 1]), W, 1e4, start_pos=int(kv[b]) - T)
+        assert np.array_equal(got[b], chunk[0])
+
+
+# ---------------------------------------- next rows: bidirectional spans ---
+
+def _span_end(S, spans):
+    e = np.arange(S, dtype=np.int32)
+    for a, b in spans:  # [a, b] inclusive
+        e[a:b + 1] = b
+    return e
+
+
+@pytest.mark.parametrize("W", [0, 5])
+def test_bidirectional_spans_match_explicit_mask(orc, W):
+    """Queries inside a span see the whole span (earlier and later keys of it)
+    plus the usual causal / window keys: against torch SDPA with the mask
+    built from the span list by a direct index test."""
+    import torch
+    B, S, Hq, Hkv, D, theta = 1, 24, 2, 1, 32, 1e4
+    spans = [(3, 8), (15, 20)]
+    q = bf16((B, S, Hq, D), [926, W, 0])
+    k = bf16((B, Hkv, S, D), [926, W, 1])
+    v = bf16((B, Hkv, S, D), [926, W, 2])
+    se = _span_end(S, spans)[None, :]
+    got = orc.prefill(q, k, v, W, theta, span_end=se)
+    span_of = {i: n for n, (a, b) in enumerate(spans) for i in range(a, b + 1)}
+    mask = np.zeros((S, S), bool)
+    for i in range(S):
+        for j in range(S):
+            same = i in span_of and span_of.get(j) == span_of[i]
+            mask[i, j] = (j <= i or same) and (W == 0 or i - j < W)
+    kr = _rot_complex(widen(k), np.arange(S)[None, None, :], theta)
+    qr = _rot_complex(widen(q).transpose(0, 2, 1, 3), np.arange(S)[None, None, :], theta)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.ascontiguousarray(qr)), torch.from_numpy(np.repeat(kr, Hq, axis=1).copy()),
+        torch.from_numpy(np.repeat(widen(v), Hq, axis=1).copy()), attn_mask=torch.from_numpy(mask))
+    assert np.max(np.abs(got - out.numpy().transpose(0, 2, 1, 3))) < 1e-10
+    # no spans is the causal prefill, bit for bit
+    assert np.array_equal(orc.prefill(q, k, v, W, theta, span_end=np.arange(S, dtype=np.int32)[None, :]),
+                          orc.prefill(q, k, v, W, theta))
+
+
+def test_one_span_over_everything_is_unmasked_attention(orc):
+    """A single span covering the whole prompt: every query sees every key
+    (closed form: torch SDPA without any mask)."""
+    import torch
+    S, D = 12, 16
+    q = bf16((1, S, 1, D), [927, 0])
+    k = bf16((1, 1, S, D), [927, 1])
+    got = orc.prefill(q, k, None, 0, 1e4, span_end=np.full((1, S), S - 1, np.int32))
+    kr = _rot_complex(widen(k), np.arange(S)[None, None, :], 1e4)
+    qr = _rot_complex(widen(q).transpose(0, 2, 1, 3), np.arange(S)[None, None, :], 1e4)
+    out = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(np.ascontiguousarray(qr)),
+                                                           torch.from_numpy(kr), torch.from_numpy(widen(k)))
+    assert np.max(np.abs(got - out.numpy().transpose(0, 2, 1, 3))) < 1e-10
