@@ -33,7 +33,9 @@ EXPORTED = (
     "gemma4_attn_prefill",
     "gemma4_attn_decode",
     "gemma4_set_profile_events",
+    "gemma4_attn_decode_noalloc",
 )
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class LayerDesc(ctypes.Structure):
@@ -81,8 +83,10 @@ def load():
     lib.gemma4_attn_prefill.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), i32, i32, i32, vp, vp, sz, vp]
     lib.gemma4_attn_decode.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), vp, i32, i32, i32, vp, vp, sz, vp]
     lib.gemma4_set_profile_events.argtypes = [vp, vp]
+    lib.gemma4_attn_decode_noalloc.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), vp, i32, i32, i32, vp, vp]
     for name in ("gemma4_set_profile_events", "gemma4_validate_layers", "gemma4_kv_bytes", "gemma4_prefill_workspace_bytes",
-                 "gemma4_decode_workspace_bytes", "gemma4_attn_prefill", "gemma4_attn_decode"):
+                 "gemma4_decode_workspace_bytes", "gemma4_attn_prefill", "gemma4_attn_decode",
+                 "gemma4_attn_decode_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -272,4 +276,28 @@ class Stack:
         _check(load().gemma4_attn_decode(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
                                          int(max_kv_len), _ptr(out), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), int(s.cuda_stream)))
+        return out
+
+    def decode_noalloc(self, layer: int, q, k_caches, v_caches, kv_len, max_kv_len: int, out, stream=None):
+        """Decode into a caller-given ``out`` using the library's static device
+        scratch (no workspace, no allocation by the library or here)."""
+        import torch
+        d = self.layers[layer]
+        B, Hq, D = q.shape
+        src = self.source(layer)
+        k = k_caches[src]
+        if k is None:
+            raise ValueError("k_caches[%d] is None" % src)
+        Lmax = k.shape[2]
+        _check_tensor(q, "q", torch.bfloat16, (B, d["num_q_heads"], d["head_dim"]))
+        _check_tensor(k, "k_cache", torch.bfloat16, (B, d["num_kv_heads"], Lmax, d["head_dim"]))
+        if not d["kv_alias"]:
+            _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
+        _check_tensor(kv_len, "kv_len", torch.int32, (B,))
+        _check_tensor(out, "out", torch.float32, (B, Hq, D))
+        s = _resolve_stream(stream)
+        kt = _ptr_table(list(k_caches))
+        vt = _ptr_table(list(v_caches)) if v_caches is not None else None
+        _check(load().gemma4_attn_decode_noalloc(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
+                                                 int(max_kv_len), _ptr(out), int(s.cuda_stream)))
         return out

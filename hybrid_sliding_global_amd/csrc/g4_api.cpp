@@ -201,10 +201,13 @@ G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers,
   return ok();
 }
 
-G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
-                                 void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
-                                 int32_t max_len, int32_t max_kv_len, float* out, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks and launch of one decode call; `workspace` NULL means the static
+// device scratch (checked against its size before anything touches the GPU).
+int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q, void* const* k_cache,
+                void* const* v_cache, const int32_t* kv_len, int32_t batch, int32_t max_len, int32_t max_kv_len,
+                float* out, void* workspace, size_t workspace_bytes, void* stream, bool use_static) {
   int rc = check_layer(layers, n_layers, layer);
   if (rc) return rc;
   const g4_layer_desc& d = layers[layer];
@@ -222,8 +225,15 @@ G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, 
   const int W = d.kind == G4_SLIDING ? d.window : 0;
   const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, W, max_kv_len);
   const size_t need = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, plan);
-  if (!workspace || workspace_bytes < need)
+  if (use_static) {
+    if (need > g4::kStaticScratchBytes)
+      return fail(G4_ERR_WORKSPACE, "decode needs %zu bytes of scratch, the static scratch holds %zu", need,
+                  g4::kStaticScratchBytes);
+    const hipError_t e = g4::static_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess) return fail(G4_ERR_HIP, "static scratch: %s", hipGetErrorString(e));
+  } else if (!workspace || workspace_bytes < need) {
     return fail(G4_ERR_WORKSPACE, "decode workspace %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
+  }
   g4::DecodeLaunch p;
   p.q = q;
   p.k = k;
@@ -244,6 +254,24 @@ G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, 
   const hipError_t e = g4::launch_decode(p, static_cast<hipStream_t>(stream), g_profile);
   if (e != hipSuccess) return fail(G4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                 void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
+                                 int32_t max_len, int32_t max_kv_len, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len, out, workspace,
+                     workspace_bytes, stream, false);
+}
+
+G4_EXPORT int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                         void* const* k_cache, void* const* v_cache, const int32_t* kv_len,
+                                         int32_t batch, int32_t max_len, int32_t max_kv_len, float* out,
+                                         void* stream) {
+  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len, out, nullptr, 0,
+                     stream, true);
 }
 
 G4_EXPORT int gemma4_set_profile_events(void* before, void* after) {

@@ -86,4 +86,12 @@ struct DecodeLaunch {
 
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const ProfileEvents& ev);
 
+// Device scratch of kStaticScratchBytes (a file-scope device array, one per
+// GPU) for the decode entry point that allocates nothing: its device address
+// on the current device, looked up on first use.  Fails with
+// hipErrorInvalidDevice if `stream` belongs to another device than the
+// current one.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(hipStream_t stream, void** ptr);
+
 }  // namespace g4

@@ -34,6 +34,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "g4_internal.h"
@@ -2608,6 +2609,42 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
       hipLaunchKernelGGL((k_decode_combine<256, 16>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a, p.out);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------- static device scratch --
+// Decode scratch for callers that cannot allocate device memory: a
+// file-scope device array, one copy per GPU the library runs on (it lives
+// until the process ends).  Host code never passes the array's name to a
+// kernel: that is a host-side stand-in, not a device address.  Its device
+// address is looked up once per device, with that device current, and kept.
+
+namespace {
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if ((int)sdev != cur) return hipErrorInvalidDevice;  // the lookup needs the stream's device current
+  }
+  if (cur < 0 || cur >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[cur] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[cur] = p;
+  }
+  *ptr = g_scratch_ptr[cur];
+  return hipSuccess;
 }
 
 }  // namespace g4

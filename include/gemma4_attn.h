@@ -216,6 +216,33 @@ int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t la
                        void* stream);
 
 /*
+ * Bytes of the device scratch gemma4_attn_decode_noalloc uses in place of a
+ * workspace: a static array the library holds on every GPU it runs on.
+ */
+#define G4_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * Decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc); no passage of the pages defines it.  Same
+ * arguments, semantics and results as gemma4_attn_decode, except that the
+ * split-K partials go to G4_STATIC_SCRATCH_BYTES of static device scratch
+ * instead of a caller workspace.  The library allocates nothing: the
+ * scratch is a file-scope device array (one per GPU, held until the process
+ * ends) whose address is looked up once per device on the first call.
+ *   - G4_ERR_WORKSPACE if the call needs more scratch than that
+ *     (gemma4_decode_workspace_bytes() > G4_STATIC_SCRATCH_BYTES);
+ *   - G4_ERR_HIP if `stream` belongs to another device than the calling
+ *     thread's current device;
+ *   - every call on one GPU shares that GPU's scratch and leaves the last
+ *     call's partials in it: calls that may overlap on one GPU (different
+ *     streams, or threads) race and must be serialised by the caller.
+ */
+int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                               void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
+                               int32_t max_len, int32_t max_kv_len, float* out, void* stream);
+
+/*
  * Profiling aid (not part of the attention computation; no passage of the
  * pages defines it).  After this call, each compute call made on the
  * calling thread records `before` on its stream immediately before

@@ -232,3 +232,16 @@ def test_compute_calls_reject_bad_arguments_without_gpu(lib):
     # layer index out of range
     assert lib.gemma4_attn_prefill(arr, n, n, fake, tab, tab, 1, 16, 16, fake, fake, 1 << 20, None) \
         == L.G4_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_oversize_calls_without_gpu(lib):
+    """The scratch-size check of the no-allocation decode runs before anything
+    touches the GPU."""
+    d = L.descs([wl.layer_desc(wl.FULL, 512, 16, 1, 1e6, 0, 0)])
+    fake = ctypes.c_void_p(0x1000)
+    tab = (ctypes.c_void_p * 1)(0x2000)
+    need = L.decode_workspace_bytes([wl.layer_desc(wl.FULL, 512, 16, 1, 1e6, 0, 0)], 0, 600, 64)
+    assert need > L.STATIC_SCRATCH_BYTES
+    assert lib.gemma4_attn_decode_noalloc(d, 1, 0, fake, tab, tab, fake, 600, 64, 64, fake, None) \
+        == L.G4_ERR_WORKSPACE
+    assert "static scratch" in L.last_error()
