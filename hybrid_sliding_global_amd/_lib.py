@@ -34,6 +34,10 @@ EXPORTED = (
     "gemma4_attn_decode",
     "gemma4_set_profile_events",
     "gemma4_attn_decode_noalloc",
+    "gemma4_prefill_ext_workspace_bytes",
+    "gemma4_attn_prefill_ext",
+    "gemma4_decode_ext_workspace_bytes",
+    "gemma4_attn_decode_ext",
 )
 STATIC_SCRATCH_BYTES = 32 << 20
 
@@ -50,6 +54,14 @@ class LayerDesc(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("rope_theta", ctypes.c_double),
     ]
+
+
+class PrefillOpts(ctypes.Structure):
+    _fields_ = [("start_pos", ctypes.c_int32), ("span_end", ctypes.c_void_p)]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p)]
 
 
 class Gemma4Error(RuntimeError):
@@ -84,9 +96,16 @@ def load():
     lib.gemma4_attn_decode.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), vp, i32, i32, i32, vp, vp, sz, vp]
     lib.gemma4_set_profile_events.argtypes = [vp, vp]
     lib.gemma4_attn_decode_noalloc.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), vp, i32, i32, i32, vp, vp]
+    lib.gemma4_prefill_ext_workspace_bytes.argtypes = [P(LayerDesc), i32, i32, i32, i32, P(PrefillOpts), P(sz)]
+    lib.gemma4_attn_prefill_ext.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), i32, i32, i32, P(PrefillOpts), vp,
+                                            vp, sz, vp]
+    lib.gemma4_decode_ext_workspace_bytes.argtypes = [P(LayerDesc), i32, i32, i32, i32, P(DecodeOpts), P(sz)]
+    lib.gemma4_attn_decode_ext.argtypes = [P(LayerDesc), i32, i32, vp, P(vp), P(vp), vp, i32, i32, i32, P(DecodeOpts),
+                                           vp, vp, sz, vp]
     for name in ("gemma4_set_profile_events", "gemma4_validate_layers", "gemma4_kv_bytes", "gemma4_prefill_workspace_bytes",
                  "gemma4_decode_workspace_bytes", "gemma4_attn_prefill", "gemma4_attn_decode",
-                 "gemma4_attn_decode_noalloc"):
+                 "gemma4_attn_decode_noalloc", "gemma4_prefill_ext_workspace_bytes", "gemma4_attn_prefill_ext",
+                 "gemma4_decode_ext_workspace_bytes", "gemma4_attn_decode_ext"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -210,18 +229,30 @@ class Stack:
         s = self.layers[layer]["kv_source_layer"]
         return layer if s < 0 else s
 
-    def prefill_workspace_bytes(self, layer: int, batch: int, seq_len: int) -> int:
+    def prefill_workspace_bytes(self, layer: int, batch: int, seq_len: int, start_pos: int = 0) -> int:
         n = ctypes.c_size_t()
-        _check(load().gemma4_prefill_workspace_bytes(self.arr, len(self), layer, batch, seq_len, ctypes.byref(n)))
+        if start_pos == 0:
+            _check(load().gemma4_prefill_workspace_bytes(self.arr, len(self), layer, batch, seq_len, ctypes.byref(n)))
+        else:
+            o = PrefillOpts(int(start_pos), None)
+            _check(load().gemma4_prefill_ext_workspace_bytes(self.arr, len(self), layer, batch, seq_len,
+                                                             ctypes.byref(o), ctypes.byref(n)))
         return n.value
 
-    def decode_workspace_bytes(self, layer: int, batch: int, max_kv_len: int) -> int:
+    def decode_workspace_bytes(self, layer: int, batch: int, max_kv_len: int, n_tokens: int = 1) -> int:
         n = ctypes.c_size_t()
-        _check(load().gemma4_decode_workspace_bytes(self.arr, len(self), layer, batch, max_kv_len, ctypes.byref(n)))
+        if n_tokens == 1:
+            _check(load().gemma4_decode_workspace_bytes(self.arr, len(self), layer, batch, max_kv_len,
+                                                        ctypes.byref(n)))
+        else:
+            o = DecodeOpts(int(n_tokens), None, None)
+            _check(load().gemma4_decode_ext_workspace_bytes(self.arr, len(self), layer, batch, max_kv_len,
+                                                            ctypes.byref(o), ctypes.byref(n)))
         return n.value
 
-    def prefill(self, layer: int, q, k_caches, v_caches, out=None, workspace=None, stream=None):
-        """q: bf16 [B,S,Hq,D]; k_caches/v_caches: per-layer lists (None for shared / aliased entries)."""
+    def prefill(self, layer: int, q, k_caches, v_caches, out=None, workspace=None, stream=None, start_pos: int = 0):
+        """q: bf16 [B,S,Hq,D] at positions start_pos .. start_pos+S-1; k_caches/v_caches:
+        per-layer lists (None for shared / aliased entries)."""
         import torch
         d = self.layers[layer]
         B, S, Hq, D = q.shape
@@ -238,44 +269,64 @@ class Stack:
         if out is None:
             out = _alloc_on(s, (B, S, Hq, D), torch.float32, q.device)
         _check_tensor(out, "out", torch.float32, (B, S, Hq, D))
-        need = self.prefill_workspace_bytes(layer, B, S)
+        need = self.prefill_workspace_bytes(layer, B, S, start_pos)
         if workspace is None:
             workspace = _alloc_on(s, (need,), torch.uint8, q.device)
         kt = _ptr_table(list(k_caches))
         vt = _ptr_table(list(v_caches)) if v_caches is not None else None
-        _check(load().gemma4_attn_prefill(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax, _ptr(out),
-                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                          int(s.cuda_stream)))
+        nbytes = workspace.numel() * workspace.element_size()
+        if start_pos == 0:
+            _check(load().gemma4_attn_prefill(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax, _ptr(out),
+                                              _ptr(workspace), nbytes, int(s.cuda_stream)))
+        else:
+            o = PrefillOpts(int(start_pos), None)
+            _check(load().gemma4_attn_prefill_ext(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax,
+                                                  ctypes.byref(o), _ptr(out), _ptr(workspace), nbytes,
+                                                  int(s.cuda_stream)))
         return out
 
     def decode(self, layer: int, q, k_caches, v_caches, kv_len, max_kv_len: int, out=None, workspace=None,
                stream=None):
-        """q: bf16 [B,Hq,D]; kv_len: int32 device [B]; max_kv_len: host bound on kv_len."""
+        """q: bf16 [B,Hq,D] (one token per sequence) or [B,T,Hq,D] (T tokens at
+        positions kv_len-T .. kv_len-1); kv_len: int32 device [B]; max_kv_len:
+        host bound on kv_len.  The output has q's shape, in fp32."""
         import torch
         d = self.layers[layer]
-        B, Hq, D = q.shape
+        multi = q.dim() == 4
+        if multi:
+            B, T, Hq, D = q.shape
+        else:
+            (B, Hq, D), T = q.shape, 1
         src = self.source(layer)
         k = k_caches[src]
         if k is None:
             raise ValueError("k_caches[%d] is None" % src)
         Lmax = k.shape[2]
-        _check_tensor(q, "q", torch.bfloat16, (B, d["num_q_heads"], d["head_dim"]))
+        qshape = (B, T, d["num_q_heads"], d["head_dim"]) if multi else (B, d["num_q_heads"], d["head_dim"])
+        _check_tensor(q, "q", torch.bfloat16, qshape)
         _check_tensor(k, "k_cache", torch.bfloat16, (B, d["num_kv_heads"], Lmax, d["head_dim"]))
         if not d["kv_alias"]:
             _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
         _check_tensor(kv_len, "kv_len", torch.int32, (B,))
         s = _resolve_stream(stream)
         if out is None:
-            out = _alloc_on(s, (B, Hq, D), torch.float32, q.device)
-        _check_tensor(out, "out", torch.float32, (B, Hq, D))
-        need = self.decode_workspace_bytes(layer, B, max_kv_len)
+            out = _alloc_on(s, tuple(q.shape), torch.float32, q.device)
+        _check_tensor(out, "out", torch.float32, tuple(q.shape))
+        need = self.decode_workspace_bytes(layer, B, max_kv_len, T)
         if workspace is None:
             workspace = _alloc_on(s, (need,), torch.uint8, q.device)
         kt = _ptr_table(list(k_caches))
         vt = _ptr_table(list(v_caches)) if v_caches is not None else None
-        _check(load().gemma4_attn_decode(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
-                                         int(max_kv_len), _ptr(out), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), int(s.cuda_stream)))
+        nbytes = workspace.numel() * workspace.element_size()
+        if not multi:
+            _check(load().gemma4_attn_decode(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
+                                             int(max_kv_len), _ptr(out), _ptr(workspace), nbytes,
+                                             int(s.cuda_stream)))
+        else:
+            o = DecodeOpts(int(T), None, None)
+            _check(load().gemma4_attn_decode_ext(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
+                                                 int(max_kv_len), ctypes.byref(o), _ptr(out), _ptr(workspace),
+                                                 nbytes, int(s.cuda_stream)))
         return out
 
     def decode_noalloc(self, layer: int, q, k_caches, v_caches, kv_len, max_kv_len: int, out, stream=None):

@@ -88,9 +88,6 @@ float resolved_scale(const g4_layer_desc& d) {
   return d.scale > 0.f ? d.scale : (float)(1.0 / std::sqrt((double)d.head_dim));
 }
 
-// The decode kernel maps the query heads of one kv head onto the 16 columns
-// of a 16x16x32 MFMA.
-constexpr int kMaxDecodeGroup = 16;
 
 }  // namespace
 
@@ -137,38 +134,85 @@ G4_EXPORT int gemma4_kv_bytes(const g4_layer_desc* layers, int32_t n_layers, int
   return ok();
 }
 
-G4_EXPORT int gemma4_prefill_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
-                                             int32_t batch, int32_t seq_len, size_t* bytes) {
+namespace {
+
+const g4_prefill_opts kPrefillDefaults = {0, nullptr};
+const g4_decode_opts kDecodeDefaults = {1, nullptr, nullptr};
+
+int check_prefill_opts(const g4_prefill_opts& o) {
+  if (o.start_pos < 0) return fail(G4_ERR_INVALID_ARG, "start_pos %d", o.start_pos);
+  if (o.span_end) return fail(G4_ERR_UNSUPPORTED, "bidirectional spans are not supported");
+  return G4_OK;
+}
+
+int check_decode_opts(const g4_decode_opts& o) {
+  if (o.n_tokens < 1) return fail(G4_ERR_INVALID_ARG, "n_tokens %d", o.n_tokens);
+  if (o.k_new || o.v_new) return fail(G4_ERR_UNSUPPORTED, "appending keys and values is not supported");
+  return G4_OK;
+}
+
+int prefill_ws(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch, int32_t seq_len,
+               const g4_prefill_opts& o, size_t* bytes) {
   int rc = check_layer(layers, n_layers, layer);
   if (rc) return rc;
   if (!bytes) return fail(G4_ERR_INVALID_ARG, "bytes is NULL");
   if (batch < 1 || seq_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d", batch, seq_len);
+  if ((rc = check_prefill_opts(o))) return rc;
   const g4_layer_desc& d = layers[layer];
   *bytes = g4::prefill_workspace(batch, seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim,
-                                 d.kind == G4_SLIDING ? d.window : 0);
+                                 d.kind == G4_SLIDING ? d.window : 0, o.start_pos);
   return ok();
 }
 
-G4_EXPORT int gemma4_decode_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
-                                            int32_t batch, int32_t max_kv_len, size_t* bytes) {
+int decode_ws(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch, int32_t max_kv_len,
+              const g4_decode_opts& o, size_t* bytes) {
   int rc = check_layer(layers, n_layers, layer);
   if (rc) return rc;
   if (!bytes) return fail(G4_ERR_INVALID_ARG, "bytes is NULL");
   if (batch < 1 || max_kv_len < 1) return fail(G4_ERR_INVALID_ARG, "batch %d, max_kv_len %d", batch, max_kv_len);
+  if ((rc = check_decode_opts(o))) return rc;
   const g4_layer_desc& d = layers[layer];
   const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, d.window, max_kv_len);
-  *bytes = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, plan);
+  *bytes = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, o.n_tokens, plan);
   return ok();
 }
 
-G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
-                                  void* const* k_cache, void* const* v_cache, int32_t batch, int32_t seq_len,
-                                  int32_t max_len, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // namespace
+
+G4_EXPORT int gemma4_prefill_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
+                                             int32_t batch, int32_t seq_len, size_t* bytes) {
+  return prefill_ws(layers, n_layers, layer, batch, seq_len, kPrefillDefaults, bytes);
+}
+
+G4_EXPORT int gemma4_prefill_ext_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
+                                                 int32_t batch, int32_t seq_len, const g4_prefill_opts* opts,
+                                                 size_t* bytes) {
+  return prefill_ws(layers, n_layers, layer, batch, seq_len, opts ? *opts : kPrefillDefaults, bytes);
+}
+
+G4_EXPORT int gemma4_decode_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
+                                            int32_t batch, int32_t max_kv_len, size_t* bytes) {
+  return decode_ws(layers, n_layers, layer, batch, max_kv_len, kDecodeDefaults, bytes);
+}
+
+G4_EXPORT int gemma4_decode_ext_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer,
+                                                int32_t batch, int32_t max_kv_len, const g4_decode_opts* opts,
+                                                size_t* bytes) {
+  return decode_ws(layers, n_layers, layer, batch, max_kv_len, opts ? *opts : kDecodeDefaults, bytes);
+}
+
+namespace {
+
+int prefill_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q, void* const* k_cache,
+                 void* const* v_cache, int32_t batch, int32_t seq_len, int32_t max_len, const g4_prefill_opts& o,
+                 float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_layer(layers, n_layers, layer);
   if (rc) return rc;
+  if ((rc = check_prefill_opts(o))) return rc;
   const g4_layer_desc& d = layers[layer];
-  if (batch < 1 || seq_len < 1 || max_len < seq_len)
-    return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d, max_len %d", batch, seq_len, max_len);
+  if (batch < 1 || seq_len < 1 || (long long)o.start_pos + seq_len > max_len)
+    return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d, start_pos %d, max_len %d", batch, seq_len, o.start_pos,
+                max_len);
   if ((long long)seq_len * (d.num_q_heads / d.num_kv_heads) > 0x7fffffffLL)
     return fail(G4_ERR_INVALID_ARG, "seq_len %d too large", seq_len);
   if (!q || !out || !k_cache) return fail(G4_ERR_INVALID_ARG, "q/out/k_cache is NULL");
@@ -178,7 +222,7 @@ G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers,
   if (!k) return fail(G4_ERR_INVALID_ARG, "k_cache[%d] is NULL", src);
   if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
   const size_t need = g4::prefill_workspace(batch, seq_len, d.num_q_heads, d.num_kv_heads, d.head_dim,
-                                            d.kind == G4_SLIDING ? d.window : 0);
+                                            d.kind == G4_SLIDING ? d.window : 0, o.start_pos);
   if (!workspace || workspace_bytes < need)
     return fail(G4_ERR_WORKSPACE, "prefill workspace %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
   g4::PrefillLaunch p;
@@ -194,11 +238,29 @@ G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers,
   p.D = d.head_dim;
   p.Lmax = max_len;
   p.W = d.kind == G4_SLIDING ? d.window : 0;
+  p.P0 = o.start_pos;
   p.scale = resolved_scale(d);
   p.theta = d.rope_theta;
   const hipError_t e = g4::launch_prefill(p, static_cast<hipStream_t>(stream), g_profile);
   if (e != hipSuccess) return fail(G4_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+G4_EXPORT int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                  void* const* k_cache, void* const* v_cache, int32_t batch, int32_t seq_len,
+                                  int32_t max_len, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_call(layers, n_layers, layer, q, k_cache, v_cache, batch, seq_len, max_len, kPrefillDefaults, out,
+                      workspace, workspace_bytes, stream);
+}
+
+G4_EXPORT int gemma4_attn_prefill_ext(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                      void* const* k_cache, void* const* v_cache, int32_t batch, int32_t seq_len,
+                                      int32_t max_len, const g4_prefill_opts* opts, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return prefill_call(layers, n_layers, layer, q, k_cache, v_cache, batch, seq_len, max_len,
+                      opts ? *opts : kPrefillDefaults, out, workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -207,15 +269,15 @@ namespace {
 // device scratch (checked against its size before anything touches the GPU).
 int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q, void* const* k_cache,
                 void* const* v_cache, const int32_t* kv_len, int32_t batch, int32_t max_len, int32_t max_kv_len,
-                float* out, void* workspace, size_t workspace_bytes, void* stream, bool use_static) {
+                const g4_decode_opts& o, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                bool use_static) {
   int rc = check_layer(layers, n_layers, layer);
   if (rc) return rc;
+  if ((rc = check_decode_opts(o))) return rc;
   const g4_layer_desc& d = layers[layer];
-  if (batch < 1 || max_kv_len < 1 || max_len < max_kv_len)
-    return fail(G4_ERR_INVALID_ARG, "batch %d, max_len %d, max_kv_len %d", batch, max_len, max_kv_len);
-  if (d.num_q_heads / d.num_kv_heads > kMaxDecodeGroup)
-    return fail(G4_ERR_UNSUPPORTED, "decode supports at most %d query heads per kv head (got %d)", kMaxDecodeGroup,
-                d.num_q_heads / d.num_kv_heads);
+  if (batch < 1 || max_kv_len < o.n_tokens || max_len < max_kv_len)
+    return fail(G4_ERR_INVALID_ARG, "batch %d, max_len %d, max_kv_len %d, n_tokens %d", batch, max_len, max_kv_len,
+                o.n_tokens);
   if (!q || !out || !k_cache || !kv_len) return fail(G4_ERR_INVALID_ARG, "q/out/k_cache/kv_len is NULL");
   const int src = source_of(layers, layer);
   const void* k = k_cache[src];
@@ -224,7 +286,7 @@ int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, co
   if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
   const int W = d.kind == G4_SLIDING ? d.window : 0;
   const g4::DecodePlan plan = g4::plan_decode(batch, d.num_kv_heads, W, max_kv_len);
-  const size_t need = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, plan);
+  const size_t need = g4::decode_workspace(batch, d.num_q_heads, d.num_kv_heads, d.head_dim, o.n_tokens, plan);
   if (use_static) {
     if (need > g4::kStaticScratchBytes)
       return fail(G4_ERR_WORKSPACE, "decode needs %zu bytes of scratch, the static scratch holds %zu", need,
@@ -248,6 +310,7 @@ int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, co
   p.Lmax = max_len;
   p.W = W;
   p.alias = d.kv_alias;
+  p.T = o.n_tokens;
   p.scale = resolved_scale(d);
   p.theta = d.rope_theta;
   p.plan = plan;
@@ -262,16 +325,24 @@ G4_EXPORT int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, 
                                  void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
                                  int32_t max_len, int32_t max_kv_len, float* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len, out, workspace,
-                     workspace_bytes, stream, false);
+  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len,
+                     kDecodeDefaults, out, workspace, workspace_bytes, stream, false);
+}
+
+G4_EXPORT int gemma4_attn_decode_ext(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                                     void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
+                                     int32_t max_len, int32_t max_kv_len, const g4_decode_opts* opts, float* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len,
+                     opts ? *opts : kDecodeDefaults, out, workspace, workspace_bytes, stream, false);
 }
 
 G4_EXPORT int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
                                          void* const* k_cache, void* const* v_cache, const int32_t* kv_len,
                                          int32_t batch, int32_t max_len, int32_t max_kv_len, float* out,
                                          void* stream) {
-  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len, out, nullptr, 0,
-                     stream, true);
+  return decode_call(layers, n_layers, layer, q, k_cache, v_cache, kv_len, batch, max_len, max_kv_len,
+                     kDecodeDefaults, out, nullptr, 0, stream, true);
 }
 
 G4_EXPORT int gemma4_set_profile_events(void* before, void* after) {

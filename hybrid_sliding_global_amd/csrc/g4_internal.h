@@ -41,7 +41,7 @@ struct PrefillPlan {
   size_t kimg_bytes = 0, vimg_off = 0, counters_off = 0, ncounters = 0, part_off = 0, slot_bytes = 0, nslots = 0,
          total = 0;
 };
-PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W);
+PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W, int P0);
 
 struct PrefillLaunch {
   const void* q;      // bf16 [B, S, Hq, D]
@@ -50,6 +50,7 @@ struct PrefillLaunch {
   float* out;         // fp32 [B, S, Hq, D]
   void* kimg;         // workspace (operand images, counters, partial slots)
   int B, S, Hq, Hkv, D, Lmax, W;
+  int P0;             // position of query 0: queries P0 .. P0+S-1 over keys 0 .. P0+S-1
   float scale;        // softmax scale (already resolved, > 0)
   double theta;
 };
@@ -60,7 +61,7 @@ struct ProfileEvents {
   hipEvent_t after = nullptr;
 };
 
-size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W);
+size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W, int P0);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const ProfileEvents& ev);
 
 // Decode split: the visible keys of all (batch, kv-head) streams are cut
@@ -69,16 +70,17 @@ struct DecodePlan {
   int npieces;  // work-groups (pieces of at least 64 keys; fewer when the keys are few)
 };
 DecodePlan plan_decode(int B, int Hkv, int W, int max_kv_len);
-size_t decode_workspace(int B, int Hq, int Hkv, int D, const DecodePlan& plan);
+size_t decode_workspace(int B, int Hq, int Hkv, int D, int T, const DecodePlan& plan);
 
 struct DecodeLaunch {
-  const void* q;        // bf16 [B, Hq, D]
+  const void* q;        // bf16 [B, T, Hq, D]
   const void* k;        // bf16 raw keys [B, Hkv, Lmax, D]
   const void* v;        // bf16 values (== k when aliased)
   const int32_t* kv_len;  // device [B]
-  float* out;           // fp32 [B, Hq, D]
+  float* out;           // fp32 [B, T, Hq, D]
   void* ws;
   int B, Hq, Hkv, D, Lmax, W, alias;
+  int T;                // query tokens per sequence (positions kv_len - T .. kv_len - 1)
   float scale;
   double theta;
   DecodePlan plan;

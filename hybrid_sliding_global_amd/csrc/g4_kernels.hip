@@ -278,7 +278,8 @@ __device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsi
 //     matches where the score layout leaves each probability).
 //
 // Values are not rotated (for an aliased layer `v` is the raw key buffer).
-// Rows at or beyond S are written as zeros.  Also clears the attention
+// Keys 0 .. nkeys-1 are imaged (a chunk at start position P0 of S queries
+// sees nkeys = P0 + S); rows at or beyond nkeys are written as zeros.  Also clears the attention
 // kernel's arrival counters (this launch precedes it on the same stream).
 //
 // Grid (2 * ntiles, Hkv, B): even work-groups write a tile's key image, odd
@@ -287,9 +288,9 @@ __device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsi
 // than one per loop step.
 template <int D, int BN>
 __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                      uint16_t* __restrict__ kimg, uint16_t* __restrict__ vimg, int S,
-                                                      int Hkv, int Lmax, int ntiles, RopeRev rope, int* counters,
-                                                      int ncounters) {
+                                                      uint16_t* __restrict__ kimg, uint16_t* __restrict__ vimg,
+                                                      int nkeys, int Hkv, int Lmax, int ntiles, RopeRev rope,
+                                                      int* counters, int ncounters) {
   constexpr int KSTEPS = D / 16, DB = D / 32, KV = BN / 16;
   constexpr int PITCH = D + 8;  // staged value row, bf16 elements (16-byte skew per row)
   constexpr int CH = D / 16;    // 16-byte chunks per half key row
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int p = t * BN + row0 + j * (256 / CH);
-      const uint16_t* r = ksrc + (size_t)min(p, S - 1) * D;  // rows past S load row S-1, then become zeros
+      const uint16_t* r = ksrc + (size_t)min(p, nkeys - 1) * D;  // rows past the keys load the last, then become zeros
       x[j] = *reinterpret_cast<const u32x4*>(r + 8 * c);
       y[j] = *reinterpret_cast<const u32x4*>(r + D / 2 + 8 * c);
     }
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict
     for (int j = 0; j < NK; ++j) {
       const int row = row0 + j * (256 / CH), p = t * BN + row;
       rope8(x[j], y[j], rev, 0, (double)p, 1.0f);
-      if (p >= S) {
+      if (p >= nkeys) {
         x[j] = u32x4{0, 0, 0, 0};
         y[j] = u32x4{0, 0, 0, 0};
       }
@@ -342,12 +343,12 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int it = threadIdx.x + 256 * j, row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
-    x[j] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)min(p, S - 1) * D + 8 * c);
+    x[j] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)min(p, nkeys - 1) * D + 8 * c);
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int it = threadIdx.x + 256 * j, row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
-    *reinterpret_cast<u32x4*>(sv + row * PITCH + 8 * c) = p < S ? x[j] : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(sv + row * PITCH + 8 * c) = p < nkeys ? x[j] : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
 #pragma unroll
@@ -375,6 +376,7 @@ struct PrefillArgs {
   int* counters;  // [B * Hkv * nqt] arrival counts (zeroed by the key pass)
   float* part;    // partial-result slots
   int B, S, Hq, Hkv, g, Lmax, W, ntiles, nqt, npair, kpieces;
+  int P0;      // position of query 0 (keys 0 .. P0 + S - 1 are visible to the chunk)
   int paired;  // 1: work unit = query tiles t and nqt-1-t; 0: one query tile
   float qscale;  // softmax scale * log2(e): scores come out in log2 units
   RopeRev rope;
@@ -443,7 +445,7 @@ k_prefill(PrefillArgs a) {
 
   auto tile_keys = [&](int qt, int& jlo, int& jhi) {
     const int r0 = qt * 128;
-    const int pmin = r0 / a.g, pmax = min(r0 + 127, rows_total - 1) / a.g;
+    const int pmin = a.P0 + r0 / a.g, pmax = a.P0 + min(r0 + 127, rows_total - 1) / a.g;
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = pmax / BN;
   };
@@ -487,9 +489,10 @@ k_prefill(PrefillArgs a) {
     const int r = r0 + rg * 32 + n;
     const bool valid = r < rows_total;
     const int rc = valid ? r : rows_total - 1;
-    const int pos = rc / a.g, head = kvh * a.g + rc % a.g;
-    const int pos_min = r0 / a.g;
-    const int pos_max = min(r0 + 127, rows_total - 1) / a.g;
+    const int sq = rc / a.g, head = kvh * a.g + rc % a.g;  // query index within the chunk
+    const int pos = a.P0 + sq;                               // its position in the sequence
+    const int pos_min = a.P0 + r0 / a.g;
+    const int pos_max = a.P0 + min(r0 + 127, rows_total - 1) / a.g;
 
     // Q' = RoPE(q) * scale * log2(e), as the B operand of S^T = K' Q'^T:
     // lane (n, h) holds head-dim elements 16*ks + 8*h + [0, 8) of its query
@@ -497,7 +500,7 @@ k_prefill(PrefillArgs a) {
     // sit in k-steps ks and ks + KSTEPS/2.
     bf16x8 qf[KSW];
     {
-      const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
+      const uint16_t* qrow = a.q + (((size_t)b * a.S + sq) * a.Hq + head) * D;
 #pragma unroll
       for (int i = 0; i < KSW / 2; ++i) {
         const int ks = dp * (KSW / 2) + i;  // first-half step, partner ks + KSTEPS/2
@@ -1056,7 +1059,7 @@ k_prefill(PrefillArgs a) {
     const float l = l_i + __shfl_xor(l_i, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (valid) {
-      float* orow = a.out + (((size_t)b * a.S + pos) * a.Hq + head) * D + 32 * dp * DBW;
+      float* orow = a.out + (((size_t)b * a.S + sq) * a.Hq + head) * D + 32 * dp * DBW;
 #pragma unroll
       for (int db = 0; db < DBW; ++db)
 #pragma unroll
@@ -1171,7 +1174,7 @@ k_prefill4(PrefillArgs a) {
 
   auto tile_keys = [&](int qt, int& jlo, int& jhi) {
     const int r0 = qt * ROWS;
-    const int pmin = r0 / a.g, pmax = min(r0 + ROWS - 1, rows_total - 1) / a.g;
+    const int pmin = a.P0 + r0 / a.g, pmax = a.P0 + min(r0 + ROWS - 1, rows_total - 1) / a.g;
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = pmax / BN;
   };
@@ -1213,9 +1216,10 @@ k_prefill4(PrefillArgs a) {
     const int r0 = qt * ROWS;
     const int r = r0 + wave * SR + (R64 ? j16 : n);  // this lane's score row
     const int rc = r < rows_total ? r : rows_total - 1;
-    const int pos = rc / a.g;
-    const int pos_min = r0 / a.g;
-    const int pos_max = min(r0 + ROWS - 1, rows_total - 1) / a.g;
+    const int sq = rc / a.g;     // query index within the chunk
+    const int pos = a.P0 + sq;   // its position in the sequence
+    const int pos_min = a.P0 + r0 / a.g;
+    const int pos_max = a.P0 + min(r0 + ROWS - 1, rows_total - 1) / a.g;
     const int nt = je - jb + 1;
 
     // The first two key tiles and the first value tile of a pass, issued
@@ -1236,7 +1240,7 @@ k_prefill4(PrefillArgs a) {
     auto qchunk = [&](int i) { return R64 ? 32 * i + 8 * grp : 16 * i + 8 * h; };
     {
       const int head = kvh * a.g + rc % a.g;
-      const uint16_t* qrow = a.q + (((size_t)b * a.S + pos) * a.Hq + head) * D;
+      const uint16_t* qrow = a.q + (((size_t)b * a.S + sq) * a.Hq + head) * D;
       // The g query heads of a position share its rotation, so when the
       // tile's positions fit, each (position, frequency) pair's cos / sin is
       // computed once by the work-group into LDS (the idle tile buffers) and
@@ -1870,13 +1874,16 @@ k_prefill4(PrefillArgs a) {
 // ---------------------------------------------------------------- decode --
 
 struct DecodeArgs {
-  const uint16_t* q;
+  const uint16_t* q;  // [B, T, Hq, D]
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* kv_len;
-  float* part_o;    // [slots][g][D]: slot = stream + piece (see k_decode)
-  float* part_lse;  // [slots][g], log2 units
+  float* part_o;    // [slots][cols][D]: slot = stream + piece (see k_decode)
+  float* part_lse;  // [slots][cols], log2 units
   int B, Hq, Hkv, g, Lmax, W;
+  int T;            // query tokens per sequence, at positions kv_len - T .. kv_len - 1
+  int ncg;          // column groups per (batch, kv head): the T*g queries in groups of 16
+  int cols;         // query columns per partial slot (T*g if one group, else 16)
   int npieces;      // work-groups of the split (pieces of the total key work)
   float qscale;
   RopeRev rope;
@@ -1938,11 +1945,17 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
-// Visible key count of batch entry b's streams (all its kv heads).
+// Cache length of batch entry b, clamped to [T, Lmax] (no access out of bounds
+// whatever kv_len holds).
+__device__ __forceinline__ int decode_len(const DecodeArgs& a, int b) { return min(max(a.kv_len[b], a.T), a.Lmax); }
+// First key any of the T queries of a length-L sequence sees.
+__device__ __forceinline__ int decode_lo(const DecodeArgs& a, int L) {
+  return a.W > 0 ? max(0, L - a.T + 1 - a.W) : 0;
+}
+// Visible key count of batch entry b's streams (all its kv heads and column groups).
 __device__ __forceinline__ long long decode_batch_keys(const DecodeArgs& a, int b) {
-  const int L = min(max(a.kv_len[b], 1), a.Lmax);
-  const int lo = a.W > 0 ? max(0, L - a.W) : 0;
-  return (long long)a.Hkv * (L - lo);
+  const int L = decode_len(a, b);
+  return (long long)a.Hkv * a.ncg * (L - decode_lo(a, L));
 }
 
 // Sum over the work-group (256 threads) of one value per thread.
@@ -2032,7 +2045,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, G = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool qvalid = n < a.g;
 
   // The visible keys of all (batch, kv-head) streams, laid end to end
   // (batch-major, kv heads of a batch entry adjacent, each stream its window
@@ -2048,10 +2060,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   if (piece >= np) return;
   const long long r0 = (long long)piece * T / np, r1 = (long long)(piece + 1) * T / np;
 
-  auto segment = [&](int b, int kvh, int k_start, int k_end, int slot) __attribute__((always_inline)) {
-  const int L = min(max(a.kv_len[b], 1), a.Lmax);
-  const int head = kvh * a.g + (qvalid ? n : 0);
-  const size_t part = (size_t)slot * a.g + (qvalid ? n : 0);
+  auto segment = [&](int b, int kvh, int cg, int k_start, int k_end, int slot) __attribute__((always_inline)) {
+  const int L = decode_len(a, b);
+  // MFMA column n is query column c = 16 cg + n of this (batch, kv head):
+  // token t = c / g at position L - T + t, head kvh * g + c % g.
+  const int c = cg * 16 + n;
+  const bool qvalid = n < a.cols && c < a.T * a.g;
+  const int ct = qvalid ? c / a.g : 0, hh = qvalid ? c % a.g : 0;
+  const int head = kvh * a.g + hh;
+  const int P = L - a.T + ct;  // this column's query position
+  const size_t part = (size_t)slot * a.cols + (qvalid ? n : 0);
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   auto issue = [&](int step, int stg) {
     int ln = lane;
@@ -2099,7 +2117,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   float ux[KH][8], uy[KH][8], stc[KH][8], sts[KH][8];
   u32x4 qx[KH], qy[KH];  // raw query pairs (bf16) of this lane
   {
-    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + head) * D;
+    const uint16_t* qrow = a.q + (((size_t)b * a.T + ct) * a.Hq + head) * D;
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int d0 = wave * FQ + 32 * kk + 8 * G;
@@ -2129,7 +2147,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
       }
     }
   };
-  anchor((double)(L - 1 - k_start));
+  anchor((double)(P - k_start));
 
   f32x4 acc[DBLK];
 #pragma unroll
@@ -2138,7 +2156,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 
   for (int s = 0; s < nsteps; ++s) {
     const int stg = s % NSTAGE;
-    if (s > 0 && s % kReanchorSteps == 0) anchor((double)(L - 1 - k_start - s * KPS));
+    if (s > 0 && s % kReanchorSteps == 0) anchor((double)(P - k_start - s * KPS));
     // Q' for this step (bf16), then advance u by R_{-16} for the next one.
     bf16x8 qf[KSTEPS];
 #pragma unroll
@@ -2198,12 +2216,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
            __builtin_bit_cast(f32x4, t[3]);
     }
 
-    // keys k0 + 4*G + jj for query n
+    // keys k0 + 4*G + jj for query column n: visible up to its own position
+    // and, for a window, back to P - W + 1 (the segment lies inside the
+    // union of the T queries' key ranges)
     float mx = kNegInf;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int key = k0 + 4 * G + jj;
-      sc[jj] = key < k_end ? sc[jj] : kNegInf;
+      const bool vis = key < k_end && key <= P && (a.W == 0 || P - key < a.W);
+      sc[jj] = vis ? sc[jj] : kNegInf;
       mx = fmaxf(mx, sc[jj]);
     }
     mx = max_over_groups(mx);
@@ -2245,30 +2266,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
     }
   }
 
+  // (a column can see no key of a segment: with T > 1 the keys after its
+  // position, or before its window; its partial is then 0 with weight 0)
   const float l = sum_over_groups(l_i);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   if (qvalid) {
     float* o = a.part_o + part * D + wave * DQ + 4 * G;
 #pragma unroll
     for (int bi = 0; bi < DBLK; ++bi) *reinterpret_cast<f32x4*>(o + 16 * bi) = acc[bi] * inv;
-    if (wave == 0 && G == 0) a.part_lse[part] = m_i + __builtin_amdgcn_logf(l);
+    if (wave == 0 && G == 0) a.part_lse[part] = l > 0.f ? m_i + __builtin_amdgcn_logf(l) : kNegInf;
   }
   lds_barrier();  // the stages are refilled by the next segment
   };
 
-  // Segments of this piece: streams from the one holding key r0 on.
+  // Segments of this piece: streams (batch, kv head, column group) from the
+  // one holding key r0 on.
   long long base = base_lo;
   for (int b = b_lo; b < a.B && base < r1; ++b) {
-    const int L = min(max(a.kv_len[b], 1), a.Lmax);
-    const int lo = a.W > 0 ? max(0, L - a.W) : 0;
+    const int L = decode_len(a, b);
+    const int lo = decode_lo(a, L);
     const int span = L - lo;
-    for (int kvh = 0; kvh < a.Hkv; ++kvh) {
-      const long long s0 = base + (long long)kvh * span, s1 = s0 + span;
+    for (int st = 0; st < a.Hkv * a.ncg; ++st) {
+      const long long s0 = base + (long long)st * span, s1 = s0 + span;
       const long long x0 = max(s0, r0), x1 = min(s1, r1);
       if (x0 < x1)
-        segment(b, kvh, lo + (int)(x0 - s0), lo + (int)(x1 - s0), b * a.Hkv + kvh + piece);
+        segment(b, st / a.ncg, st % a.ncg, lo + (int)(x0 - s0), lo + (int)(x1 - s0),
+                (b * a.Hkv) * a.ncg + st + piece);
     }
-    base += (long long)a.Hkv * span;
+    base += (long long)a.Hkv * a.ncg * span;
   }
 }
 
@@ -2291,8 +2316,11 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __r
   __shared__ float sden[NGRP][NQ];
   __shared__ float smax[4];
   __shared__ long long s_red[4];
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq, head = bh % a.Hq, kvh = head / a.g, hg = head % a.g;
+  const int bh = blockIdx.x;  // (batch, token, head)
+  const int head = bh % a.Hq, bt = bh / a.Hq, tok = bt % a.T, b = bt / a.T;
+  const int kvh = head / a.g;
+  const int c = tok * a.g + head % a.g;        // query column of this (batch, kv head)
+  const int cg = c / 16, n = c - 16 * cg;      // its column group and slot column (one group: cg 0, n = c)
   const int qd = threadIdx.x % NQ, grp = threadIdx.x / NQ;
   // total keys, and the keys of the streams before this batch entry's
   long long t = 0, tb = 0;
@@ -2304,12 +2332,13 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __r
   const long long T = block_sum_ll(t, s_red);
   const long long base_b = block_sum_ll(tb, s_red);
   const int np = (int)min((long long)a.npieces, max(1LL, T / 64));
-  const long long span = decode_batch_keys(a, b) / a.Hkv;
-  const long long x0 = base_b + (long long)kvh * span, x1 = x0 + span;  // this stream's keys
+  const long long span = decode_batch_keys(a, b) / (a.Hkv * a.ncg);
+  const int stream = (b * a.Hkv + kvh) * a.ncg + cg;
+  const long long x0 = base_b + (long long)(kvh * a.ncg + cg) * span, x1 = x0 + span;  // this stream's keys
   const int p0 = (int)(((x0 + 1) * np - 1) / T), p1 = (int)((x1 * np - 1) / T);  // pieces holding x0, x1 - 1
   const int npart = p1 - p0 + 1;
-  const size_t first = (size_t)(b * a.Hkv + kvh + p0) * a.g + hg;  // partial k at first + k * g
-  auto pidx = [&](int k) { return first + (size_t)k * a.g; };
+  const size_t first = (size_t)(stream + p0) * a.cols + n;  // partial k at first + k * cols
+  auto pidx = [&](int k) { return first + (size_t)k * a.cols; };
   const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + blockIdx.y * NQ + qd;
   // This thread's first U partials (grp, grp + NGRP, ...) are loaded before
   // the largest log-sum-exp is known, so both take one memory round trip.
@@ -2356,6 +2385,8 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __r
     num += w * po[pidx(k) * (D / 4)];
     den += w;
   }
+  // (partials of segments the query sees no key of have log-sum-exp -inf:
+  // weight 0, value 0)
   snum[grp][qd] = num;
   sden[grp][qd] = den;
   __syncthreads();
@@ -2381,10 +2412,10 @@ void fill_rope_rev(RopeRev* r, int head_dim, double theta) {
     r->rev[f] = f < head_dim / 2 ? std::pow(theta, -2.0 * (double)f / (double)head_dim) / two_pi : 0.0;
 }
 
-// Key tiles a 128-row query tile visits (same rule as the kernel).
-static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int rows, int& jlo, int& jhi) {
+// Key tiles a query tile visits (same rule as the kernel; P0 = position of query 0).
+static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int rows, int P0, int& jlo, int& jhi) {
   const int rows_total = S * g, r0 = qt * rows;
-  const int pmin = r0 / g, pmax = std::min(r0 + rows - 1, rows_total - 1) / g;
+  const int pmin = P0 + r0 / g, pmax = P0 + std::min(r0 + rows - 1, rows_total - 1) / g;
   jlo = (W > 0 ? std::max(0, pmin - W + 1) : 0) / BN;
   jhi = pmax / BN;
 }
@@ -2428,10 +2459,10 @@ static int prefill_split_pv_override() {
   return (v == 0 || v == 1) ? v : -1;
 }
 
-PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
+PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W, int P0) {
   PrefillPlan p;
   p.BN = prefill_key_tile(D);
-  p.ntiles = ceil_div(S, p.BN);
+  p.ntiles = ceil_div(P0 + S, p.BN);
   p.g = Hq / Hkv;
   const int forced = D == 256 ? prefill_rows_override() : 0;
   double best = 0.0;
@@ -2448,10 +2479,10 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
       for (int i = 0; i < nunits; ++i) {
         int a0, a1, b0 = 0, b1 = -1;
         if (paired) {
-          prefill_tile_keys(nqt - 1 - i, S, p.g, W, p.BN, rows, a0, a1);
-          if (i < nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, rows, b0, b1);
+          prefill_tile_keys(nqt - 1 - i, S, p.g, W, p.BN, rows, P0, a0, a1);
+          if (i < nqt - 1 - i) prefill_tile_keys(i, S, p.g, W, p.BN, rows, P0, b0, b1);
         } else {
-          prefill_tile_keys(i, S, p.g, W, p.BN, rows, a0, a1);
+          prefill_tile_keys(i, S, p.g, W, p.BN, rows, P0, a0, a1);
         }
         umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
       }
@@ -2493,10 +2524,12 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W) {
   return p;
 }
 
-size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W) { return plan_prefill(B, S, Hq, Hkv, D, W).total; }
+size_t prefill_workspace(int B, int S, int Hq, int Hkv, int D, int W, int P0) {
+  return plan_prefill(B, S, Hq, Hkv, D, W, P0).total;
+}
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const ProfileEvents& ev) {
-  const PrefillPlan pl = plan_prefill(p.B, p.S, p.Hq, p.Hkv, p.D, p.W);
+  const PrefillPlan pl = plan_prefill(p.B, p.S, p.Hq, p.Hkv, p.D, p.W, p.P0);
   char* ws = static_cast<char*>(p.kimg);
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(p.q);
@@ -2507,6 +2540,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   a.part = reinterpret_cast<float*>(ws + pl.part_off);
   a.B = p.B;
   a.S = p.S;
+  a.P0 = p.P0;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.g = pl.g;
@@ -2526,7 +2560,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   uint16_t* kimg = reinterpret_cast<uint16_t*>(ws);
   uint16_t* vimg = reinterpret_cast<uint16_t*>(ws + pl.vimg_off);
   if (p.D == 512) {
-    hipLaunchKernelGGL((k_prefill_prep<512, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
+    hipLaunchKernelGGL((k_prefill_prep<512, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.P0 + p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     if (pl.split_pv)
@@ -2534,7 +2568,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
     else
       hipLaunchKernelGGL((k_prefill<512, 32, 2, false>), grid_a, dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.S, p.Hkv,
+    hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.P0 + p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     if (pl.rows == 64)
@@ -2557,9 +2591,18 @@ DecodePlan plan_decode(int /*B*/, int /*Hkv*/, int /*W*/, int /*max_kv_len*/) {
   return plan;
 }
 
-size_t decode_workspace(int B, int Hq, int Hkv, int D, const DecodePlan& plan) {
-  // one partial per (stream + piece) slot and query head of the group
-  const size_t parts = ((size_t)B * Hkv + plan.npieces) * (size_t)(Hq / Hkv);
+// Query columns of one (batch, kv head): T tokens x g heads, in groups of 16
+// (the N dimension of the decode MFMAs); each group is a stream of its own.
+static void decode_columns(int T, int g, int& ncg, int& cols) {
+  ncg = ceil_div(T * g, 16);
+  cols = ncg == 1 ? T * g : 16;
+}
+
+size_t decode_workspace(int B, int Hq, int Hkv, int D, int T, const DecodePlan& plan) {
+  // one partial per (stream + piece) slot and query column of the stream
+  int ncg, cols;
+  decode_columns(T, Hq / Hkv, ncg, cols);
+  const size_t parts = ((size_t)B * Hkv * ncg + plan.npieces) * (size_t)cols;
   return parts * D * sizeof(float) + parts * sizeof(float);
 }
 
@@ -2569,7 +2612,9 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   a.k = static_cast<const uint16_t*>(p.k);
   a.v = static_cast<const uint16_t*>(p.alias ? p.k : p.v);
   a.kv_len = p.kv_len;
-  const size_t parts = ((size_t)p.B * p.Hkv + p.plan.npieces) * (size_t)(p.Hq / p.Hkv);
+  a.T = p.T;
+  decode_columns(p.T, p.Hq / p.Hkv, a.ncg, a.cols);
+  const size_t parts = ((size_t)p.B * p.Hkv * a.ncg + p.plan.npieces) * (size_t)a.cols;
   a.part_o = static_cast<float*>(p.ws);
   a.part_lse = a.part_o + parts * p.D;
   a.B = p.B;
@@ -2596,17 +2641,19 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   // Streams of few pieces: one work-group per head; of many: 64-wide slices.
-  const bool wide = p.plan.npieces / (p.B * p.Hkv) + 1 <= kCombineWideMaxParts;
+  const int nstreams = p.B * p.Hkv * a.ncg;
+  const bool wide = p.plan.npieces / nstreams + 1 <= kCombineWideMaxParts;
+  const unsigned nq = (unsigned)(p.B * p.T * p.Hq);
   if (p.D == 512) {
     if (wide)
-      hipLaunchKernelGGL((k_decode_combine<512, 128>), dim3(p.B * p.Hq), dim3(256), 0, stream, a, p.out);
+      hipLaunchKernelGGL((k_decode_combine<512, 128>), dim3(nq), dim3(256), 0, stream, a, p.out);
     else
-      hipLaunchKernelGGL((k_decode_combine<512, 16>), dim3(p.B * p.Hq, 512 / 64), dim3(256), 0, stream, a, p.out);
+      hipLaunchKernelGGL((k_decode_combine<512, 16>), dim3(nq, 512 / 64), dim3(256), 0, stream, a, p.out);
   } else {
     if (wide)
-      hipLaunchKernelGGL((k_decode_combine<256, 64>), dim3(p.B * p.Hq), dim3(256), 0, stream, a, p.out);
+      hipLaunchKernelGGL((k_decode_combine<256, 64>), dim3(nq), dim3(256), 0, stream, a, p.out);
     else
-      hipLaunchKernelGGL((k_decode_combine<256, 16>), dim3(p.B * p.Hq, 256 / 64), dim3(256), 0, stream, a, p.out);
+      hipLaunchKernelGGL((k_decode_combine<256, 16>), dim3(nq, 256 / 64), dim3(256), 0, stream, a, p.out);
   }
   return hipGetLastError();
 }

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define G4_ABI_VERSION 1
+#define G4_ABI_VERSION 2
 
 /* Status codes (library plumbing; no passage of the pages defines them). */
 #define G4_OK 0
@@ -208,7 +208,6 @@ int gemma4_attn_prefill(const g4_layer_desc* layers, int32_t n_layers, int32_t l
  *              device, so it needs no host copy of the lengths)
  *   out        fp32 [batch, Hq, head_dim]
  *   workspace  device scratch of at least gemma4_decode_workspace_bytes()
- * Requires Hq / Hkv <= 16.
  */
 int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
                        void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
@@ -241,6 +240,83 @@ int gemma4_attn_decode(const g4_layer_desc* layers, int32_t n_layers, int32_t la
 int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
                                void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
                                int32_t max_len, int32_t max_kv_len, float* out, void* stream);
+
+/*
+ * Options of gemma4_attn_prefill_ext: queries against a cache that already
+ * holds earlier positions.  [SG] MTP paragraph (a draft reading the
+ * target's frozen KV cache, FROZEN_KV_MTP) and [FR] "What Would Need to
+ * Change" item 2 (the runtime's KV cache management) ask for attention
+ * over an existing cache; a prompt processed in chunks is the same call.
+ *   start_pos  position of query 0: the call's seq_len queries sit at
+ *              positions start_pos .. start_pos + seq_len - 1 and see cache
+ *              rows 0 .. start_pos + seq_len - 1 (all written by the
+ *              caller); 0 is a whole prompt
+ *   span_end   reserved: must be NULL
+ */
+typedef struct {
+  int32_t start_pos;
+  const int32_t* span_end;
+} g4_prefill_opts;
+
+/*
+ * Options of gemma4_attn_decode_ext.
+ *   n_tokens   T >= 1 queries per sequence at positions kv_len[b] - T ..
+ *              kv_len[b] - 1, each seeing the cache up to its own position
+ *              (T > 1: the verify step of speculative decoding over a
+ *              frozen cache, [SG] MTP paragraph, FROZEN_KV_MTP); their keys
+ *              and values must already be in the cache
+ *   k_new      reserved: must be NULL
+ *   v_new      reserved: must be NULL
+ */
+typedef struct {
+  int32_t n_tokens;
+  const void* k_new;
+  const void* v_new;
+} g4_decode_opts;
+
+/* Workspace bytes of gemma4_attn_prefill_ext (opts NULL: as
+ * gemma4_prefill_workspace_bytes).  The operation it serves is cited at
+ * gemma4_attn_prefill_ext. */
+int gemma4_prefill_ext_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch,
+                                       int32_t seq_len, const g4_prefill_opts* opts, size_t* bytes);
+
+/*
+ * Prefill of a chunk of queries against a cache holding the earlier
+ * positions -- [SG] MTP paragraph (attention over a frozen cache), [FR]
+ * "What Would Need to Change" item 2; otherwise as gemma4_attn_prefill.
+ *   q          bf16 [batch, seq_len, Hq, head_dim], raw (pre-RoPE), query s
+ *              at position start_pos + s
+ *   k_cache    rows 0 .. start_pos + seq_len - 1 written by the caller
+ *   out        fp32 [batch, seq_len, Hq, head_dim]
+ * Requires start_pos + seq_len <= max_len.  opts NULL = start_pos 0.
+ */
+int gemma4_attn_prefill_ext(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                            void* const* k_cache, void* const* v_cache, int32_t batch, int32_t seq_len,
+                            int32_t max_len, const g4_prefill_opts* opts, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of gemma4_attn_decode_ext (opts NULL: as
+ * gemma4_decode_workspace_bytes).  The operation it serves is cited at
+ * gemma4_attn_decode_ext. */
+int gemma4_decode_ext_workspace_bytes(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, int32_t batch,
+                                      int32_t max_kv_len, const g4_decode_opts* opts, size_t* bytes);
+
+/*
+ * Decode of n_tokens queries per sequence over its cache -- [SG] MTP
+ * paragraph (the verify step over a frozen KV cache); otherwise as
+ * gemma4_attn_decode.
+ *   q          bf16 [batch, n_tokens, Hq, head_dim], raw; token t of
+ *              sequence b at position kv_len[b] - n_tokens + t
+ *   kv_len     device int32 [batch], n_tokens <= kv_len[b] <= max_kv_len
+ *              (values outside are clamped: undefined results, no
+ *              out-of-bounds access)
+ *   out        fp32 [batch, n_tokens, Hq, head_dim]
+ * Requires n_tokens <= max_kv_len <= max_len.  opts NULL = one token.
+ */
+int gemma4_attn_decode_ext(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, const void* q,
+                           void* const* k_cache, void* const* v_cache, const int32_t* kv_len, int32_t batch,
+                           int32_t max_len, int32_t max_kv_len, const g4_decode_opts* opts, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Profiling aid (not part of the attention computation; no passage of the

@@ -68,7 +68,7 @@ def test_every_header_declaration_cites_its_passage():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
     for code, name in [(0, "G4_OK"), (-1, "G4_ERR_INVALID_ARG"), (-2, "G4_ERR_UNSUPPORTED"),
                        (-3, "G4_ERR_BAD_SOURCE"), (-4, "G4_ERR_WORKSPACE"), (-5, "G4_ERR_HIP")]:
         assert L.status_string(code) == name
@@ -189,6 +189,12 @@ def test_workspace_sizes(lib):
     # one fp32 partial (head_dim values and a log-sum-exp) per query head for
     # every stream plus every piece of the split: (B*Hkv + 512) * g * (D + 1) * 4
     assert w == (64 * 2 + 512) * 4 * (512 + 1) * 4
+    # T query tokens: T*g columns per (batch, kv head), in groups of 16
+    st = L.Stack(stack)
+    assert st.decode_workspace_bytes(4, 64, 8192, 3) == (64 * 2 + 512) * 12 * (512 + 1) * 4
+    assert st.decode_workspace_bytes(4, 64, 8192, 5) == (64 * 2 * 2 + 512) * 16 * (512 + 1) * 4
+    # a chunk at start position P0 images keys 0 .. P0 + S - 1
+    assert st.prefill_workspace_bytes(0, 1, 64, 1000) >= 2 * (1064 + 31) // 32 * 32 * 256 * 2
     with pytest.raises(L.Gemma4Error):
         L.prefill_workspace_bytes(stack, 4, 0, 2048)
 
@@ -224,9 +230,23 @@ def test_compute_calls_reject_bad_arguments_without_gpu(lib):
         == L.G4_ERR_INVALID_ARG
     assert lib.gemma4_attn_decode(arr, n, 4, fake, tab, tab, None, 4, 100, 100, fake, fake, 1 << 20, None) \
         == L.G4_ERR_INVALID_ARG
+    # 32 query heads per kv head: two groups of 16 MFMA columns, accepted (here stopped by the workspace)
     wide = L.descs([wl.layer_desc(wl.FULL, 512, 32, 1, 1e6, 0, 0)])
-    assert lib.gemma4_attn_decode(wide, 1, 0, fake, tab, tab, fake, 4, 100, 100, fake, fake, 1 << 30, None) \
-        == L.G4_ERR_UNSUPPORTED
+    assert lib.gemma4_attn_decode(wide, 1, 0, fake, tab, tab, fake, 4, 100, 100, fake, fake, 8, None) \
+        == L.G4_ERR_WORKSPACE
+    # ext calls: start_pos + seq_len beyond the cache, n_tokens above max_kv_len, reserved options set
+    po = L.PrefillOpts(10, None)
+    assert lib.gemma4_attn_prefill_ext(arr, n, 4, fake, tab, tab, 1, 16, 20, ctypes.byref(po), fake, fake, 1 << 20,
+                                       None) == L.G4_ERR_INVALID_ARG
+    po = L.PrefillOpts(0, 0x10)
+    assert lib.gemma4_attn_prefill_ext(arr, n, 4, fake, tab, tab, 1, 16, 20, ctypes.byref(po), fake, fake, 1 << 20,
+                                       None) == L.G4_ERR_UNSUPPORTED
+    do = L.DecodeOpts(5, None, None)
+    assert lib.gemma4_attn_decode_ext(arr, n, 4, fake, tab, tab, fake, 4, 100, 4, ctypes.byref(do), fake, fake,
+                                      1 << 30, None) == L.G4_ERR_INVALID_ARG
+    do = L.DecodeOpts(0, None, None)
+    assert lib.gemma4_attn_decode_ext(arr, n, 4, fake, tab, tab, fake, 4, 100, 100, ctypes.byref(do), fake, fake,
+                                      1 << 30, None) == L.G4_ERR_INVALID_ARG
     assert lib.gemma4_attn_decode(arr, n, 4, fake, tab, tab, fake, 64, 8192, 8192, fake, fake, 8, None) \
         == L.G4_ERR_WORKSPACE
     # layer index out of range

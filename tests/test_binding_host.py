@@ -24,6 +24,9 @@ class _FakeTensor:
     def data_ptr(self):
         return 0x1000
 
+    def dim(self):
+        return len(self.shape)
+
     def numel(self):
         n = 1
         for x in self.shape:

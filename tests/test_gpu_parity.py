@@ -432,3 +432,65 @@ def test_decode_long_pieces():
     rows = np.array([0 * Hq + 0, 5 * Hq + 3, 9 * Hq + 4, 15 * Hq + 7], np.int64)
     got = out.cpu().numpy().reshape(-1, D)[rows]
     check(got, oracle.decode(q, k, None, kv, 0, wl.THETA_FULL, rows=rows), "decode long pieces")
+
+
+# ------------------------------------- queries against an existing cache --
+# A chunk of a prompt at start position P0 (keys 0 .. P0+S-1 already in the
+# cache) and T > 1 decode tokens per sequence (the verify step of
+# speculative decoding over a frozen cache).
+
+@pytest.mark.parametrize("B,S,P0,Hq,Hkv,D,W,alias,override", [
+    (1, 300, 1000, 8, 2, 512, 0, False, ("G4_PREFILL_SPLIT_PV", "0")),
+    (1, 300, 1000, 8, 2, 512, 0, False, ("G4_PREFILL_SPLIT_PV", "1")),
+    (1, 128, 3968, 8, 2, 512, 0, False, None),      # the last 128 queries of the 4096-token layer
+    (2, 200, 1500, 8, 1, 256, 512, True, ("G4_PREFILL_ROWS", "64")),
+    (2, 200, 1500, 8, 1, 256, 512, True, ("G4_PREFILL_ROWS", "128")),
+    (1, 1, 37, 4, 1, 256, 0, False, None),           # one query: a decode step through the prefill path
+    (1, 77, 5, 6, 2, 512, 64, True, None),           # short history, windowed, GQA group of 3
+    (1, 640, 640, 8, 1, 256, 0, False, ("G4_PREFILL_ROWS", "128")),  # tiles cut into pieces
+])
+def test_chunked_prefill(monkeypatch, B, S, P0, Hq, Hkv, D, W, alias, override):
+    import torch
+    if override:
+        monkeypatch.setenv(*override)
+    Lmax = P0 + S + 7
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    q = inputs.normal_bf16([700, P0, 0], (B, S, Hq, D))
+    k = inputs.normal_bf16([700, P0, 1], (B, Hkv, Lmax, D))
+    v = None if alias else inputs.normal_bf16([700, P0, 2], (B, Hkv, Lmax, D))
+    k[:, :, P0 + S:] = inputs.NAN_BF16  # rows past the chunk must never be read
+    if v is not None:
+        v[:, :, P0 + S:] = inputs.NAN_BF16
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias))])
+    ws = torch.full((st.prefill_workspace_bytes(0, B, S, P0),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    out = st.prefill(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)], workspace=ws, start_pos=P0)
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), oracle.prefill(q, k, v, W, theta, start_pos=P0),
+          "chunk B%d S%d P0=%d D%d W%d %s" % (B, S, P0, D, W, override))
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,W,alias,kv_len,Lmax", [
+    (3, 2, 8, 2, 512, 0, False, [2, 700, 4096], 4096),      # T*g = 8
+    (3, 4, 8, 2, 512, 0, False, [4, 33, 3000], 3000),       # T*g = 16: one full column group
+    (2, 7, 8, 2, 512, 0, False, [5000, 7], 5000),           # T*g = 28: two column groups
+    (4, 2, 8, 1, 256, 1024, True, [2, 500, 1025, 3000], 3000),  # sliding K=V, windows of both tokens
+    (3, 3, 16, 2, 256, 64, True, [64, 65, 2000], 2048),     # T*g = 24, window smaller than the span of tokens
+    (2, 5, 4, 4, 256, 0, False, [31, 40], 40),              # no GQA sharing
+    (2, 3, 32, 1, 512, 0, False, [900, 3], 900),            # 32 query heads per kv head: six column groups
+])
+def test_multi_token_decode(B, T, Hq, Hkv, D, W, alias, kv_len, Lmax):
+    import torch
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    kv = np.asarray(kv_len, np.int32)
+    q = inputs.normal_bf16([710, T, 0], (B, T, Hq, D))
+    k = inputs.poison_beyond(inputs.normal_bf16([710, T, 1], (B, Hkv, Lmax, D)), kv)
+    v = None if alias else inputs.poison_beyond(inputs.normal_bf16([710, T, 2], (B, Hkv, Lmax, D)), kv)
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias))])
+    ws = torch.full((st.decode_workspace_bytes(0, B, Lmax, T),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    out = st.decode(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)], torch.from_numpy(kv).to("cuda:0"),
+                    Lmax, workspace=ws)
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), oracle.decode(q, k, v, kv, W, theta),
+          "decode T%d B%d Hq%d Hkv%d D%d W%d L%s" % (T, B, Hq, Hkv, D, W, kv_len))
