@@ -53,6 +53,10 @@ class LayerDesc(ctypes.Structure):
         ("kv_source_layer", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("rope_theta", ctypes.c_double),
+        ("kv_dtype", ctypes.c_int32),
+        ("kv_ring", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -142,7 +146,8 @@ def descs(layers: Sequence[dict]):
     for i, d in enumerate(layers):
         arr[i] = LayerDesc(int(d["kind"]), int(d["head_dim"]), int(d["num_q_heads"]), int(d["num_kv_heads"]),
                            int(d["window"]), int(d["kv_alias"]), int(d["kv_source_layer"]), float(d.get("scale", 0.0)),
-                           float(d["rope_theta"]))
+                           float(d["rope_theta"]), int(d.get("kv_dtype", 0)), int(d.get("kv_ring", 0)),
+                           float(d.get("k_scale", 1.0)), float(d.get("v_scale", 1.0)))
     return arr
 
 
@@ -286,10 +291,12 @@ class Stack:
         return out
 
     def decode(self, layer: int, q, k_caches, v_caches, kv_len, max_kv_len: int, out=None, workspace=None,
-               stream=None):
+               stream=None, k_new=None, v_new=None):
         """q: bf16 [B,Hq,D] (one token per sequence) or [B,T,Hq,D] (T tokens at
         positions kv_len-T .. kv_len-1); kv_len: int32 device [B]; max_kv_len:
-        host bound on kv_len.  The output has q's shape, in fp32."""
+        host bound on kv_len.  k_new / v_new: bf16 [B,T,Hkv,D] (or [B,Hkv,D]
+        for one token) keys / values of those tokens, written into the cache
+        by the call.  The output has q's shape, in fp32."""
         import torch
         d = self.layers[layer]
         multi = q.dim() == 4
@@ -308,6 +315,11 @@ class Stack:
         if not d["kv_alias"]:
             _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
         _check_tensor(kv_len, "kv_len", torch.int32, (B,))
+        if k_new is not None:
+            nshape = (B, T, d["num_kv_heads"], d["head_dim"]) if multi else (B, d["num_kv_heads"], d["head_dim"])
+            _check_tensor(k_new, "k_new", torch.bfloat16, nshape)
+            if v_new is not None:
+                _check_tensor(v_new, "v_new", torch.bfloat16, nshape)
         s = _resolve_stream(stream)
         if out is None:
             out = _alloc_on(s, tuple(q.shape), torch.float32, q.device)
@@ -318,12 +330,12 @@ class Stack:
         kt = _ptr_table(list(k_caches))
         vt = _ptr_table(list(v_caches)) if v_caches is not None else None
         nbytes = workspace.numel() * workspace.element_size()
-        if not multi:
+        if not multi and k_new is None:
             _check(load().gemma4_attn_decode(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
                                              int(max_kv_len), _ptr(out), _ptr(workspace), nbytes,
                                              int(s.cuda_stream)))
         else:
-            o = DecodeOpts(int(T), None, None)
+            o = DecodeOpts(int(T), _ptr(k_new), _ptr(v_new))
             _check(load().gemma4_attn_decode_ext(self.arr, len(self), layer, _ptr(q), kt, vt, _ptr(kv_len), B, Lmax,
                                                  int(max_kv_len), ctypes.byref(o), _ptr(out), _ptr(workspace),
                                                  nbytes, int(s.cuda_stream)))

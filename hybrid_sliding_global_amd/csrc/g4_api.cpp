@@ -54,6 +54,11 @@ int check_desc(const g4_layer_desc& d, int idx) {
   if (!(d.rope_theta > 0.0) || !std::isfinite(d.rope_theta))
     return fail(G4_ERR_INVALID_ARG, "layer %d: rope_theta %g", idx, d.rope_theta);
   if (!(d.scale >= 0.f) || !std::isfinite(d.scale)) return fail(G4_ERR_INVALID_ARG, "layer %d: scale %g", idx, d.scale);
+  if (d.kv_dtype != G4_KV_BF16) return fail(G4_ERR_UNSUPPORTED, "layer %d: kv_dtype %d", idx, d.kv_dtype);
+  if (d.kv_ring < 0) return fail(G4_ERR_INVALID_ARG, "layer %d: kv_ring %d", idx, d.kv_ring);
+  if (d.kv_ring > 0 && (d.kind != G4_SLIDING || d.kv_ring < d.window))
+    return fail(G4_ERR_INVALID_ARG, "layer %d: a ring cache (kv_ring %d) needs a sliding layer with window <= kv_ring",
+                idx, d.kv_ring);
   return G4_OK;
 }
 
@@ -77,6 +82,9 @@ int check_layer(const g4_layer_desc* layers, int32_t n_layers, int32_t idx) {
   if (src.head_dim != d.head_dim || src.num_kv_heads != d.num_kv_heads || src.kv_alias != d.kv_alias)
     return fail(G4_ERR_BAD_SOURCE, "layer %d: source layer %d has head_dim/num_kv_heads/kv_alias %d/%d/%d, needs %d/%d/%d",
                 idx, s, src.head_dim, src.num_kv_heads, src.kv_alias, d.head_dim, d.num_kv_heads, d.kv_alias);
+  if (src.kv_dtype != d.kv_dtype || src.kv_ring != d.kv_ring)
+    return fail(G4_ERR_BAD_SOURCE, "layer %d: source layer %d has kv_dtype/kv_ring %d/%d, needs %d/%d", idx, s,
+                src.kv_dtype, src.kv_ring, d.kv_dtype, d.kv_ring);
   return G4_OK;
 }
 
@@ -128,7 +136,8 @@ G4_EXPORT int gemma4_kv_bytes(const g4_layer_desc* layers, int32_t n_layers, int
     *k_bytes = *v_bytes = 0;
     return ok();
   }
-  const size_t bytes = (size_t)batch * d.num_kv_heads * (size_t)max_len * d.head_dim * 2;
+  const size_t rows = d.kv_ring > 0 ? (size_t)d.kv_ring : (size_t)max_len;  // a ring holds kv_ring rows
+  const size_t bytes = (size_t)batch * d.num_kv_heads * rows * d.head_dim * 2;
   *k_bytes = bytes;
   *v_bytes = d.kv_alias ? 0 : bytes;
   return ok();
@@ -147,7 +156,7 @@ int check_prefill_opts(const g4_prefill_opts& o) {
 
 int check_decode_opts(const g4_decode_opts& o) {
   if (o.n_tokens < 1) return fail(G4_ERR_INVALID_ARG, "n_tokens %d", o.n_tokens);
-  if (o.k_new || o.v_new) return fail(G4_ERR_UNSUPPORTED, "appending keys and values is not supported");
+  if (!o.k_new && o.v_new) return fail(G4_ERR_INVALID_ARG, "v_new given without k_new");
   return G4_OK;
 }
 
@@ -210,6 +219,8 @@ int prefill_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, c
   if (rc) return rc;
   if ((rc = check_prefill_opts(o))) return rc;
   const g4_layer_desc& d = layers[layer];
+  if (d.kv_ring > 0)
+    return fail(G4_ERR_UNSUPPORTED, "layer %d: prefill reads a cache of one row per position, not a ring", layer);
   if (batch < 1 || seq_len < 1 || (long long)o.start_pos + seq_len > max_len)
     return fail(G4_ERR_INVALID_ARG, "batch %d, seq_len %d, start_pos %d, max_len %d", batch, seq_len, o.start_pos,
                 max_len);
@@ -275,13 +286,21 @@ int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, co
   if (rc) return rc;
   if ((rc = check_decode_opts(o))) return rc;
   const g4_layer_desc& d = layers[layer];
-  if (batch < 1 || max_kv_len < o.n_tokens || max_len < max_kv_len)
+  if (batch < 1 || max_kv_len < o.n_tokens || (d.kv_ring == 0 && max_len < max_kv_len))
     return fail(G4_ERR_INVALID_ARG, "batch %d, max_len %d, max_kv_len %d, n_tokens %d", batch, max_len, max_kv_len,
                 o.n_tokens);
+  if (d.kv_ring > 0 && max_len != d.kv_ring)
+    return fail(G4_ERR_INVALID_ARG, "layer %d: a ring cache of %d rows, max_len %d", layer, d.kv_ring, max_len);
+  if (d.kv_ring > 0 && (long long)d.window + o.n_tokens - 1 > d.kv_ring)
+    return fail(G4_ERR_INVALID_ARG, "layer %d: %d tokens with window %d need a ring of %d rows (has %d)", layer,
+                o.n_tokens, d.window, d.window + o.n_tokens - 1, d.kv_ring);
+  if (o.k_new && d.kv_alias && o.v_new)
+    return fail(G4_ERR_INVALID_ARG, "layer %d: v_new given for a K=V layer", layer);
+  if (o.k_new && !d.kv_alias && !o.v_new) return fail(G4_ERR_INVALID_ARG, "layer %d: v_new missing", layer);
   if (!q || !out || !k_cache || !kv_len) return fail(G4_ERR_INVALID_ARG, "q/out/k_cache/kv_len is NULL");
   const int src = source_of(layers, layer);
-  const void* k = k_cache[src];
-  const void* v = d.kv_alias ? k : (v_cache ? v_cache[src] : nullptr);
+  void* k = k_cache[src];
+  void* v = d.kv_alias ? k : (v_cache ? v_cache[src] : nullptr);
   if (!k) return fail(G4_ERR_INVALID_ARG, "k_cache[%d] is NULL", src);
   if (!v) return fail(G4_ERR_INVALID_ARG, "v_cache[%d] is NULL for a layer without K=V aliasing", src);
   const int W = d.kind == G4_SLIDING ? d.window : 0;
@@ -311,6 +330,9 @@ int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, co
   p.W = W;
   p.alias = d.kv_alias;
   p.T = o.n_tokens;
+  p.ring = d.kv_ring;
+  p.k_new = o.k_new;
+  p.v_new = d.kv_alias ? o.k_new : o.v_new;
   p.scale = resolved_scale(d);
   p.theta = d.rope_theta;
   p.plan = plan;

@@ -74,13 +74,16 @@ size_t decode_workspace(int B, int Hq, int Hkv, int D, int T, const DecodePlan& 
 
 struct DecodeLaunch {
   const void* q;        // bf16 [B, T, Hq, D]
-  const void* k;        // bf16 raw keys [B, Hkv, Lmax, D]
-  const void* v;        // bf16 values (== k when aliased)
+  void* k;              // bf16 raw keys [B, Hkv, Lmax, D] (written only when appending)
+  void* v;              // bf16 values (== k when aliased)
   const int32_t* kv_len;  // device [B]
   float* out;           // fp32 [B, T, Hq, D]
   void* ws;
   int B, Hq, Hkv, D, Lmax, W, alias;
   int T;                // query tokens per sequence (positions kv_len - T .. kv_len - 1)
+  int ring;             // 0: row j holds position j; C > 0: row j % C (Lmax == C)
+  const void* k_new;    // null, or bf16 [B, T, Hkv, D]: keys of the T tokens, written into the cache
+  const void* v_new;    // values of the T tokens (== k_new when aliased)
   float scale;
   double theta;
   DecodePlan plan;

@@ -1885,6 +1885,11 @@ struct DecodeArgs {
   int ncg;          // column groups per (batch, kv head): the T*g queries in groups of 16
   int cols;         // query columns per partial slot (T*g if one group, else 16)
   int npieces;      // work-groups of the split (pieces of the total key work)
+  int ring;         // 0: cache row j holds position j; C > 0: row j % C (a window-sized ring, Lmax = C)
+  const uint16_t* knew;  // null, or [B, T, Hkv, D]: keys of the T tokens, read in place of their cache rows
+  const uint16_t* vnew;  // their values (== knew when aliased)
+  uint16_t* kc;          // the cache, written by k_decode_combine when appending
+  uint16_t* vc;
   float qscale;
   RopeRev rope;
 };
@@ -1945,9 +1950,15 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
-// Cache length of batch entry b, clamped to [T, Lmax] (no access out of bounds
-// whatever kv_len holds).
-__device__ __forceinline__ int decode_len(const DecodeArgs& a, int b) { return min(max(a.kv_len[b], a.T), a.Lmax); }
+// Sequence length of batch entry b, clamped to [T, Lmax] for a cache of one
+// row per position (a ring maps any position into its rows), so that no
+// access goes out of bounds whatever kv_len holds.
+__device__ __forceinline__ int decode_len(const DecodeArgs& a, int b) {
+  const int L = max(a.kv_len[b], a.T);
+  return a.ring > 0 ? L : min(L, a.Lmax);
+}
+// Cache row of key position j.
+__device__ __forceinline__ int decode_row(const DecodeArgs& a, int j) { return a.ring > 0 ? j % a.ring : j; }
 // First key any of the T queries of a length-L sequence sees.
 __device__ __forceinline__ int decode_lo(const DecodeArgs& a, int L) {
   return a.W > 0 ? max(0, L - a.T + 1 - a.W) : 0;
@@ -2071,6 +2082,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   const int P = L - a.T + ct;  // this column's query position
   const size_t part = (size_t)slot * a.cols + (qvalid ? n : 0);
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
+  // Keys of the T current tokens come from the appended rows when the call
+  // writes them (k_decode_combine stores them into the cache afterwards).
+  const int new0 = a.knew != nullptr ? L - a.T : 0x7fffffff;
+  // Cache row of key position pos of this segment: row0 + (pos - k_start),
+  // wrapped once for a ring (a segment spans at most the ring's length).
+  const int wrap = a.ring > 0 ? a.ring : 0x7fffffff;
+  const int row0 = a.ring > 0 ? k_start % a.ring : k_start;
   auto issue = [&](int step, int stg) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -2078,14 +2096,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 #pragma unroll
     for (int tsr = 0; tsr < NT; ++tsr) {
       const uint16_t* base = (tsr == 0 ? a.k : a.v) + slice;
+      const uint16_t* nbase = (tsr == 0 ? a.knew : a.vnew) + ((size_t)b * a.T * a.Hkv + kvh) * D;
 #pragma unroll
       for (int i = 0; i < LPS1; ++i) {
         const int blk = i * 4 + wave;
         const int byte = blk * 1024 + ln * 16;
         const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
-        const int src_row = min(k0 + row, k_end - 1);
-        g2l16_nt(base + (size_t)src_row * D + ((slot ^ swz(row)) << 3),
-                 reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
+        const int pos = min(k0 + row, k_end - 1);  // key position
+        int crow = row0 + (pos - k_start);
+        crow = crow >= wrap ? crow - wrap : crow;
+        const uint16_t* src = pos >= new0 ? nbase + (size_t)(pos - new0) * a.Hkv * D : base + (size_t)crow * D;
+        g2l16_nt(src + ((slot ^ swz(row)) << 3), reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
       }
     }
   };
@@ -2115,33 +2136,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   // is re-anchored from the fp64 angle every kReanchorSteps steps, so its
   // fp32 drift (angle and length) is bounded whatever the segment length.
   float ux[KH][8], uy[KH][8], stc[KH][8], sts[KH][8];
-  u32x4 qx[KH], qy[KH];  // raw query pairs (bf16) of this lane
-  {
-    const uint16_t* qrow = a.q + (((size_t)b * a.T + ct) * a.Hq + head) * D;
+  const uint16_t* qrow = a.q + (((size_t)b * a.T + ct) * a.Hq + head) * D;
 #pragma unroll
-    for (int kk = 0; kk < KH; ++kk) {
-      const int d0 = wave * FQ + 32 * kk + 8 * G;
-      qx[kk] = *reinterpret_cast<const u32x4*>(qrow + d0);
-      qy[kk] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+  for (int kk = 0; kk < KH; ++kk) {
+    const int d0 = wave * FQ + 32 * kk + 8 * G;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float st = (float)KPS * (float)a.rope.rev[d0 + t];
-        st -= __builtin_rintf(st);
-        stc[kk][t] = __builtin_amdgcn_cosf(st);
-        sts[kk][t] = -__builtin_amdgcn_sinf(st);  // rotation by -KPS positions
-      }
+    for (int t = 0; t < 8; ++t) {
+      float st = (float)KPS * (float)a.rope.rev[d0 + t];
+      st -= __builtin_rintf(st);
+      stc[kk][t] = __builtin_amdgcn_cosf(st);
+      sts[kk][t] = -__builtin_amdgcn_sinf(st);  // rotation by -KPS positions
     }
   }
+  // (the raw query pairs are re-read at each anchor -- from L2, once per
+  // kReanchorSteps steps -- rather than held in registers)
   auto anchor = [&](double rel) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int d0 = wave * FQ + 32 * kk + 8 * G;
+      const u32x4 qx = *reinterpret_cast<const u32x4*>(qrow + d0);
+      const u32x4 qy = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         float sn, cn;
         sincos_rev(rel, a.rope.rev[d0 + t], sn, cn);
-        const float xa = (t & 1) ? bf_hi(qx[kk][t >> 1]) : bf_lo(qx[kk][t >> 1]);
-        const float ya = (t & 1) ? bf_hi(qy[kk][t >> 1]) : bf_lo(qy[kk][t >> 1]);
+        const float xa = (t & 1) ? bf_hi(qx[t >> 1]) : bf_lo(qx[t >> 1]);
+        const float ya = (t & 1) ? bf_hi(qy[t >> 1]) : bf_lo(qy[t >> 1]);
         ux[kk][t] = qvalid ? (xa * cn - ya * sn) * a.qscale : 0.f;
         uy[kk][t] = qvalid ? (ya * cn + xa * sn) * a.qscale : 0.f;
       }
@@ -2322,6 +2342,18 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a, float* __r
   const int c = tok * a.g + head % a.g;        // query column of this (batch, kv head)
   const int cg = c / 16, n = c - 16 * cg;      // its column group and slot column (one group: cg 0, n = c)
   const int qd = threadIdx.x % NQ, grp = threadIdx.x / NQ;
+  if (a.knew != nullptr && head % a.g == 0 && blockIdx.y == 0) {
+    // Append: the first head of each kv head stores its token's key (and
+    // value) row into the cache; k_decode, which read them from the new rows,
+    // has finished (same stream), so no reader sees a half-written row.
+    const int P = decode_len(a, b) - a.T + tok;
+    const size_t dst = ((size_t)(b * a.Hkv + kvh) * a.Lmax + decode_row(a, P)) * D;
+    const size_t src = (((size_t)b * a.T + tok) * a.Hkv + kvh) * D;
+    for (int i = threadIdx.x; i < D / 8; i += 256) {
+      reinterpret_cast<u32x4*>(a.kc + dst)[i] = reinterpret_cast<const u32x4*>(a.knew + src)[i];
+      if (a.vnew != a.knew) reinterpret_cast<u32x4*>(a.vc + dst)[i] = reinterpret_cast<const u32x4*>(a.vnew + src)[i];
+    }
+  }
   // total keys, and the keys of the streams before this batch entry's
   long long t = 0, tb = 0;
   for (int bb = threadIdx.x; bb < a.B; bb += 256) {
@@ -2611,6 +2643,11 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
   a.v = static_cast<const uint16_t*>(p.alias ? p.k : p.v);
+  a.kc = static_cast<uint16_t*>(p.k);
+  a.vc = static_cast<uint16_t*>(p.alias ? p.k : p.v);
+  a.ring = p.ring;
+  a.knew = static_cast<const uint16_t*>(p.k_new);
+  a.vnew = static_cast<const uint16_t*>(p.alias ? p.k_new : p.v_new);
   a.kv_len = p.kv_len;
   a.T = p.T;
   decode_columns(p.T, p.Hq / p.Hkv, a.ncg, a.cols);

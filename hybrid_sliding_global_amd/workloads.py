@@ -28,11 +28,16 @@ HEAD_DIM_SLIDING, HEAD_DIM_FULL = 256, 512
 THETA_SLIDING, THETA_FULL = 10000.0, 1000000.0
 
 
+KV_BF16, KV_FP8 = 0, 1
+
+
 def layer_desc(kind: int, head_dim: int, num_q_heads: int, num_kv_heads: int, rope_theta: float, window: int,
-               kv_alias: int, kv_source_layer: int = -1, scale: float = 0.0) -> dict:
+               kv_alias: int, kv_source_layer: int = -1, scale: float = 0.0, kv_dtype: int = KV_BF16,
+               kv_ring: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> dict:
     return dict(kind=int(kind), head_dim=int(head_dim), num_q_heads=int(num_q_heads), num_kv_heads=int(num_kv_heads),
                 rope_theta=float(rope_theta), window=int(window), kv_alias=int(kv_alias),
-                kv_source_layer=int(kv_source_layer), scale=float(scale))
+                kv_source_layer=int(kv_source_layer), scale=float(scale), kv_dtype=int(kv_dtype),
+                kv_ring=int(kv_ring), k_scale=float(k_scale), v_scale=float(v_scale))
 
 
 def attention_pattern(n_layers: int, period: int = 5) -> List[int]:

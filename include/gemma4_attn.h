@@ -110,6 +110,17 @@ extern "C" {
  *                   "Gemma 4 Model Details" (separate theta values for
  *                   sliding and full attention); [LD] module comment (dual
  *                   RoPE theta).
+ *   kv_dtype        element type of the layer's cache: G4_KV_BF16 (0) --
+ *                   [LD] load_layers (layer_kv_dtypes: a KV cache dtype per
+ *                   layer).  Must equal the source layer's.
+ *   kv_ring         0: the cache holds row j for position j ([batch, Hkv,
+ *                   max_len, head_dim]); C > 0: a window-sized ring of C rows
+ *                   per (batch, kv head), position j in row j mod C (sliding
+ *                   layers only, C >= window; decode only) -- [FR] "What
+ *                   Would Need to Change" item 2 (variable-size KV cache
+ *                   buffers per layer).  Must equal the source layer's.
+ *   k_scale,        reserved for 8-bit caches; ignored for G4_KV_BF16.
+ *   v_scale
  */
 typedef struct {
   int32_t kind;
@@ -121,7 +132,14 @@ typedef struct {
   int32_t kv_source_layer;
   float scale;
   double rope_theta;
+  int32_t kv_dtype;
+  int32_t kv_ring;
+  float k_scale;
+  float v_scale;
 } g4_layer_desc;
+
+/* Cache element types (kv_dtype). */
+#define G4_KV_BF16 0
 
 /* ABI version of the loaded library (G4_ABI_VERSION at build time).  Library
  * plumbing; no passage of the pages defines it. */
@@ -265,8 +283,14 @@ typedef struct {
  *              (T > 1: the verify step of speculative decoding over a
  *              frozen cache, [SG] MTP paragraph, FROZEN_KV_MTP); their keys
  *              and values must already be in the cache
- *   k_new      reserved: must be NULL
- *   v_new      reserved: must be NULL
+ *   k_new      NULL, or device bf16 [batch, n_tokens, Hkv, head_dim]: the raw
+ *              keys of the T tokens; the call writes them into the cache
+ *              (row of position kv_len[b] - T + t, modulo kv_ring for a
+ *              ring) and attends to them as if they had been there -- the
+ *              fused append a window-sized cache needs ([FR] "What Would
+ *              Need to Change" item 2)
+ *   v_new      likewise the values; NULL for an aliased layer (the keys are
+ *              the values), required otherwise when k_new is given
  */
 typedef struct {
   int32_t n_tokens;
@@ -303,8 +327,10 @@ int gemma4_decode_ext_workspace_bytes(const g4_layer_desc* layers, int32_t n_lay
 
 /*
  * Decode of n_tokens queries per sequence over its cache -- [SG] MTP
- * paragraph (the verify step over a frozen KV cache); otherwise as
- * gemma4_attn_decode.
+ * paragraph (the verify step over a frozen KV cache) -- optionally writing
+ * their keys and values into the cache first (opts->k_new), and reading a
+ * ring cache (kv_ring > 0: max_len = kv_ring, kv_len unbounded, kv_ring >=
+ * window + n_tokens - 1); otherwise as gemma4_attn_decode.
  *   q          bf16 [batch, n_tokens, Hq, head_dim], raw; token t of
  *              sequence b at position kv_len[b] - n_tokens + t
  *   kv_len     device int32 [batch], n_tokens <= kv_len[b] <= max_kv_len

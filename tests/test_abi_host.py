@@ -74,9 +74,29 @@ def test_abi_version_and_status_strings(lib):
         assert L.status_string(code) == name
 
 
-def test_descriptor_layout_matches_header(lib):
-    assert ctypes.sizeof(L.LayerDesc) == 40
-    assert L.LayerDesc.rope_theta.offset == 32 and L.LayerDesc.scale.offset == 28
+def _c_layout(struct, fields):
+    """sizeof and offsetof of a header struct, from a C program compiled against include/gemma4_attn.h."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    prog = "#include <stdio.h>\n#include <stddef.h>\n#include \"gemma4_attn.h\"\nint main(void){printf(\"%%zu\", sizeof(%s));" % struct
+    prog += "".join('printf(" %%zu", offsetof(%s, %s));' % (struct, f) for f in fields) + "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        return [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+
+
+@pytest.mark.parametrize("struct,cls", [("g4_layer_desc", "LayerDesc"), ("g4_prefill_opts", "PrefillOpts"),
+                                        ("g4_decode_opts", "DecodeOpts")])
+def test_struct_layouts_match_header(lib, struct, cls):
+    c = getattr(L, cls)
+    fields = [f[0] for f in c._fields_]
+    got = _c_layout(struct, fields)
+    assert got == [ctypes.sizeof(c)] + [getattr(c, f).offset for f in fields]
 
 
 def test_gemma4_stack_validates(lib):

@@ -494,3 +494,88 @@ def test_multi_token_decode(B, T, Hq, Hkv, D, W, alias, kv_len, Lmax):
     torch.cuda.synchronize()
     check(out.cpu().numpy(), oracle.decode(q, k, v, kv, W, theta),
           "decode T%d B%d Hq%d Hkv%d D%d W%d L%s" % (T, B, Hq, Hkv, D, W, kv_len))
+
+
+# -------------------------------- window-sized ring caches, fused append --
+# A sliding layer's cache of C >= W rows per (batch, kv head) keeps position
+# j in row j mod C; the decode call can also write the current tokens' keys
+# and values itself (into the ring or a linear cache) and attend to them.
+
+def _ring_from_linear(lin, kv, C, poison_old=0):
+    """Ring of C rows holding positions max(0, L-C) .. L-1 of each sequence;
+    rows of the ``poison_old`` oldest positions it holds are set to NaN."""
+    B, H, _, D = lin.shape
+    ring = np.full((B, H, C, D), inputs.NAN_BF16, np.uint16)
+    for b, L in enumerate(kv):
+        lo = max(0, int(L) - C)
+        for j in range(lo, int(L)):
+            ring[b, :, j % C] = lin[b, :, j]
+        for j in range(lo, min(int(L), lo + poison_old)):
+            ring[b, :, j % C] = inputs.NAN_BF16
+    return ring
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,W,C,alias,kv_len", [
+    (4, 1, 8, 1, 256, 1024, 1024, True, [5000, 1024, 1, 3000]),   # the batched sliding layer's shape, ring = window
+    (3, 1, 16, 2, 256, 1024, 1100, True, [1100, 70000, 2047]),    # spare rows hold older positions (poisoned)
+    (2, 3, 8, 2, 512, 300, 302, False, [303, 9999]),               # three tokens: ring = window + 2
+])
+def test_ring_cache_decode(B, T, Hq, Hkv, D, W, C, alias, kv_len):
+    import torch
+    kv = np.asarray(kv_len, np.int32)
+    Lmax = int(kv.max())
+    q = inputs.normal_bf16([720, C, 0], (B, T, Hq, D) if T > 1 else (B, Hq, D))
+    k = inputs.normal_bf16([720, C, 1], (B, Hkv, Lmax, D))
+    v = None if alias else inputs.normal_bf16([720, C, 2], (B, Hkv, Lmax, D))
+    spare = C - (W + T - 1)
+    kr = _ring_from_linear(k, kv, C, spare)
+    vr = None if alias else _ring_from_linear(v, kv, C, spare)
+    st = Stack([wl.layer_desc(wl.SLIDING, D, Hq, Hkv, wl.THETA_SLIDING, W, int(alias), kv_ring=C)])
+    out = st.decode(0, to_dev(q), [to_dev(kr)], [None if vr is None else to_dev(vr)],
+                    torch.from_numpy(kv).to("cuda:0"), Lmax)
+    torch.cuda.synchronize()
+    want = oracle.decode(q, kr, vr, kv, W, wl.THETA_SLIDING, ring=C)
+    assert np.array_equal(want, oracle.decode(q, k, v, kv, W, wl.THETA_SLIDING))
+    check(out.cpu().numpy(), want, "ring decode C%d T%d D%d" % (C, T, D))
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,W,C,alias,kv_len,Lmax", [
+    (3, 1, 8, 2, 512, 0, 0, False, [1, 700, 4096], 4096),       # linear full layer, one token
+    (3, 2, 8, 1, 256, 1024, 0, True, [2, 1500, 800], 1500),      # linear sliding K=V, two tokens
+    (4, 1, 8, 1, 256, 1024, 1024, True, [5000, 1024, 1, 3000], 0),  # ring = window
+    (2, 3, 8, 2, 512, 300, 310, False, [303, 9999], 0),           # ring, three tokens, separate values
+])
+def test_decode_with_fused_append(B, T, Hq, Hkv, D, W, C, alias, kv_len, Lmax):
+    """The call writes the T tokens' keys/values into the cache and attends to
+    them: its output equals the oracle's on the cache with those rows
+    written, and afterwards the device cache holds exactly that cache."""
+    import torch
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    kv = np.asarray(kv_len, np.int32)
+    rows = C if C else Lmax
+    q = inputs.normal_bf16([730, T, 0], (B, T, Hq, D) if T > 1 else (B, Hq, D))
+    kc = inputs.normal_bf16([730, T, 1], (B, Hkv, rows, D))  # stale contents everywhere
+    vc = None if alias else inputs.normal_bf16([730, T, 2], (B, Hkv, rows, D))
+    kn = inputs.normal_bf16([730, T, 3], (B, T, Hkv, D) if T > 1 else (B, Hkv, D))
+    vn = None if alias else inputs.normal_bf16([730, T, 4], (B, T, Hkv, D) if T > 1 else (B, Hkv, D))
+    # the host copy with the new rows written where the call must write them
+    kw, vw = kc.copy(), None if vc is None else vc.copy()
+    kn4 = kn.reshape(B, T, Hkv, D)
+    vn4 = None if vn is None else vn.reshape(B, T, Hkv, D)
+    for b in range(B):
+        for t in range(T):
+            r = (kv[b] - T + t) % C if C else kv[b] - T + t
+            kw[b, :, r] = kn4[b, t]
+            if vw is not None:
+                vw[b, :, r] = vn4[b, t]
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias), kv_ring=C)])
+    kd, vd = to_dev(kc), None if vc is None else to_dev(vc)
+    out = st.decode(0, to_dev(q), [kd], [vd], torch.from_numpy(kv).to("cuda:0"), int(kv.max()),
+                    k_new=to_dev(kn), v_new=None if vn is None else to_dev(vn))
+    torch.cuda.synchronize()
+    want = oracle.decode(q, kw, vw, kv, W, theta, ring=C)
+    check(out.cpu().numpy(), want, "append C%d T%d D%d" % (C, T, D))
+    assert np.array_equal(kd.cpu().view(torch.int16).numpy().view(np.uint16), kw), "key cache after the append"
+    if vd is not None:
+        assert np.array_equal(vd.cpu().view(torch.int16).numpy().view(np.uint16), vw), "value cache after the append"
