@@ -255,9 +255,11 @@ class Stack:
                                                             ctypes.byref(o), ctypes.byref(n)))
         return n.value
 
-    def prefill(self, layer: int, q, k_caches, v_caches, out=None, workspace=None, stream=None, start_pos: int = 0):
+    def prefill(self, layer: int, q, k_caches, v_caches, out=None, workspace=None, stream=None, start_pos: int = 0,
+                span_end=None):
         """q: bf16 [B,S,Hq,D] at positions start_pos .. start_pos+S-1; k_caches/v_caches:
-        per-layer lists (None for shared / aliased entries)."""
+        per-layer lists (None for shared / aliased entries); span_end: None, or
+        int32 device [B,S], the last position of each query's bidirectional span."""
         import torch
         d = self.layers[layer]
         B, S, Hq, D = q.shape
@@ -280,11 +282,13 @@ class Stack:
         kt = _ptr_table(list(k_caches))
         vt = _ptr_table(list(v_caches)) if v_caches is not None else None
         nbytes = workspace.numel() * workspace.element_size()
-        if start_pos == 0:
+        if span_end is not None:
+            _check_tensor(span_end, "span_end", torch.int32, (B, S))
+        if start_pos == 0 and span_end is None:
             _check(load().gemma4_attn_prefill(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax, _ptr(out),
                                               _ptr(workspace), nbytes, int(s.cuda_stream)))
         else:
-            o = PrefillOpts(int(start_pos), None)
+            o = PrefillOpts(int(start_pos), _ptr(span_end))
             _check(load().gemma4_attn_prefill_ext(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax,
                                                   ctypes.byref(o), _ptr(out), _ptr(workspace), nbytes,
                                                   int(s.cuda_stream)))

@@ -150,7 +150,6 @@ const g4_decode_opts kDecodeDefaults = {1, nullptr, nullptr};
 
 int check_prefill_opts(const g4_prefill_opts& o) {
   if (o.start_pos < 0) return fail(G4_ERR_INVALID_ARG, "start_pos %d", o.start_pos);
-  if (o.span_end) return fail(G4_ERR_UNSUPPORTED, "bidirectional spans are not supported");
   return G4_OK;
 }
 
@@ -250,6 +249,7 @@ int prefill_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, c
   p.Lmax = max_len;
   p.W = d.kind == G4_SLIDING ? d.window : 0;
   p.P0 = o.start_pos;
+  p.span_end = o.span_end;
   p.scale = resolved_scale(d);
   p.theta = d.rope_theta;
   const hipError_t e = g4::launch_prefill(p, static_cast<hipStream_t>(stream), g_profile);

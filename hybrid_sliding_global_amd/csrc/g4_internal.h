@@ -51,6 +51,7 @@ struct PrefillLaunch {
   void* kimg;         // workspace (operand images, counters, partial slots)
   int B, S, Hq, Hkv, D, Lmax, W;
   int P0;             // position of query 0: queries P0 .. P0+S-1 over keys 0 .. P0+S-1
+  const int32_t* span_end;  // null, or device [B, S]: last position of each query's bidirectional span
   float scale;        // softmax scale (already resolved, > 0)
   double theta;
 };

@@ -377,10 +377,24 @@ struct PrefillArgs {
   float* part;    // partial-result slots
   int B, S, Hq, Hkv, g, Lmax, W, ntiles, nqt, npair, kpieces;
   int P0;      // position of query 0 (keys 0 .. P0 + S - 1 are visible to the chunk)
+  const int32_t* span_end;  // null (causal), or [B, S]: the last position of each query's bidirectional span
   int paired;  // 1: work unit = query tiles t and nqt-1-t; 0: one query tile
   float qscale;  // softmax scale * log2(e): scores come out in log2 units
   RopeRev rope;
 };
+
+// Causal limit of query sq (at position pos) of batch entry b: the last key
+// it sees -- its own position, or the end of its bidirectional span, clamped
+// to [pos, P0 + S - 1] so that no image row beyond the chunk is ever read.
+// The limit never decreases along the positions (spans are disjoint
+// intervals), so over a query tile it is smallest at the tile's first
+// position and largest at its last.
+// Kernels instantiated without spans (SPAN = false) ignore span_end.
+template <bool SPAN>
+__device__ __forceinline__ int causal_limit(const PrefillArgs& a, int b, int sq, int pos) {
+  if constexpr (!SPAN) return pos;
+  return min(max(a.span_end[(size_t)b * a.S + sq], pos), a.P0 + a.S - 1);
+}
 
 __device__ __forceinline__ float max_lane_pair(float x) {  // max over lanes l and l ^ 32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -404,7 +418,7 @@ __device__ __forceinline__ float max_lane_pair(float x) {  // max over lanes l a
 // partial (O, running max, running sum) and bumps the tile's counter; the
 // last one merges the others into its own registers and writes the output.
 // Nobody waits for anybody.
-template <int D, int BN, int DS, bool SPV>
+template <int D, int BN, int DS, bool SPV, bool SPAN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256 * DS, 256 * DS), amdgpu_waves_per_eu(DS, DS))) void
 k_prefill(PrefillArgs a) {
   constexpr int NT = 256 * DS;                // threads
@@ -447,7 +461,7 @@ k_prefill(PrefillArgs a) {
     const int r0 = qt * 128;
     const int pmin = a.P0 + r0 / a.g, pmax = a.P0 + min(r0 + 127, rows_total - 1) / a.g;
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
-    jhi = pmax / BN;
+    jhi = causal_limit<SPAN>(a, b, pmax - a.P0, pmax) / BN;
   };
   const int tl = a.paired ? a.nqt - 1 - pair : pair;   // long tile of the pair
   const int ts = a.paired && pair < tl ? pair : -1;   // short tile (none for the middle of an odd count)
@@ -493,6 +507,8 @@ k_prefill(PrefillArgs a) {
     const int pos = a.P0 + sq;                               // its position in the sequence
     const int pos_min = a.P0 + r0 / a.g;
     const int pos_max = a.P0 + min(r0 + 127, rows_total - 1) / a.g;
+    const int lim = causal_limit<SPAN>(a, b, sq, pos);                      // this row's last visible key
+    const int lim_min = causal_limit<SPAN>(a, b, pos_min - a.P0, pos_min);  // the smallest limit of the tile
 
     // Q' = RoPE(q) * scale * log2(e), as the B operand of S^T = K' Q'^T:
     // lane (n, h) holds head-dim elements 16*ks + 8*h + [0, 8) of its query
@@ -557,14 +573,14 @@ k_prefill(PrefillArgs a) {
     // Mask and online softmax of key tile j: P^T (bf16, MFMA B-operand order) into pk.
     auto softmax = [&](int j, f32x16 (&s)[MB], unsigned (&pk)[MB * 8]) __attribute__((always_inline)) {
       const int kbase = j * BN;
-      const bool need_mask = (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
+      const bool need_mask = (kbase + BN - 1 > lim_min) || (windowed && kbase <= pos_max - a.W);
       if (need_mask) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
-            const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+            const bool vis = (key <= lim) & (!windowed | (pos - key < a.W));
             s[mb][rr] = vis ? s[mb][rr] : kNegInf;
           }
       }
@@ -1058,8 +1074,12 @@ k_prefill(PrefillArgs a) {
 
     const float l = l_i + __shfl_xor(l_i, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (valid) {
-      float* orow = a.out + (((size_t)b * a.S + sq) * a.Hq + head) * D + 32 * dp * DBW;
+    // (the row's coordinates are recomputed here rather than kept live
+    // through the tile loop, where every register is taken)
+    const int r_o = __builtin_amdgcn_readfirstlane(r0) + rg * 32 + n;
+    if (r_o < rows_total) {
+      const int sq_o = r_o / a.g, head_o = kvh * a.g + r_o % a.g;
+      float* orow = a.out + (((size_t)b * a.S + sq_o) * a.Hq + head_o) * D + 32 * dp * DBW;
 #pragma unroll
       for (int db = 0; db < DBW; ++db)
 #pragma unroll
@@ -1129,7 +1149,7 @@ __device__ __forceinline__ void mfma16v_last(f32x4& d, const bf16x8& a, const bf
 // iterations i .. i+1, P(i) in exchange buffer i&1 during i .. i+1.
 // The work split over work-groups (pairs of query tiles, pieces of their
 // key work) and the partial-result merge follow k_prefill.
-template <int D, int BN, int ROWS>
+template <int D, int BN, int ROWS, bool SPAN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 k_prefill4(PrefillArgs a) {
   static_assert(ROWS == 128 || ROWS == 64, "query tile of 128 or 64 rows");
@@ -1176,7 +1196,7 @@ k_prefill4(PrefillArgs a) {
     const int r0 = qt * ROWS;
     const int pmin = a.P0 + r0 / a.g, pmax = a.P0 + min(r0 + ROWS - 1, rows_total - 1) / a.g;
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
-    jhi = pmax / BN;
+    jhi = causal_limit<SPAN>(a, b, pmax - a.P0, pmax) / BN;
   };
   const int tl = a.paired ? a.nqt - 1 - pair : pair;
   const int ts = a.paired && pair < tl ? pair : -1;
@@ -1220,6 +1240,8 @@ k_prefill4(PrefillArgs a) {
     const int pos = a.P0 + sq;   // its position in the sequence
     const int pos_min = a.P0 + r0 / a.g;
     const int pos_max = a.P0 + min(r0 + ROWS - 1, rows_total - 1) / a.g;
+    const int lim = causal_limit<SPAN>(a, b, sq, pos);                      // this lane's row's last visible key
+    const int lim_min = causal_limit<SPAN>(a, b, pos_min - a.P0, pos_min);  // the smallest limit of the tile
     const int nt = je - jb + 1;
 
     // The first two key tiles and the first value tile of a pass, issued
@@ -1371,7 +1393,7 @@ k_prefill4(PrefillArgs a) {
     // the window's lower edge need one.
     auto needs_mask = [&](int j) {
       const int kbase = j * BN;
-      return (kbase + BN - 1 > pos_min) || (windowed && kbase <= pos_max - a.W);
+      return (kbase + BN - 1 > lim_min) || (windowed && kbase <= pos_max - a.W);
     };
     auto mask = [&](int j, SArr& s) {
       const int kbase = j * BN;
@@ -1381,7 +1403,7 @@ k_prefill4(PrefillArgs a) {
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int key = kbase + 16 * mb + 4 * grp + ii;
-            const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+            const bool vis = (key <= lim) & (!windowed | (pos - key < a.W));
             s[mb][ii] = vis ? s[mb][ii] : kNegInf;
           }
       } else {
@@ -1390,7 +1412,7 @@ k_prefill4(PrefillArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int key = kbase + 32 * mb + 8 * (rr >> 2) + 4 * h + (rr & 3);
-            const bool vis = (key <= pos) & (!windowed | (pos - key < a.W));
+            const bool vis = (key <= lim) & (!windowed | (pos - key < a.W));
             s[mb][rr] = vis ? s[mb][rr] : kNegInf;
           }
       }
@@ -2573,6 +2595,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   a.B = p.B;
   a.S = p.S;
   a.P0 = p.P0;
+  a.span_end = p.span_end;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.g = pl.g;
@@ -2595,18 +2618,31 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
     hipLaunchKernelGGL((k_prefill_prep<512, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.P0 + p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
-    if (pl.split_pv)
-      hipLaunchKernelGGL((k_prefill<512, 32, 2, true>), grid_a, dim3(512), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_prefill<512, 32, 2, false>), grid_a, dim3(512), 0, stream, a);
+    if (a.span_end != nullptr) {
+      // (spans run the split-PV schedule at every length: the other one's
+      // register allocation spills with the per-row limit added)
+      hipLaunchKernelGGL((k_prefill<512, 32, 2, true, true>), grid_a, dim3(512), 0, stream, a);
+    } else {
+      if (pl.split_pv)
+        hipLaunchKernelGGL((k_prefill<512, 32, 2, true, false>), grid_a, dim3(512), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_prefill<512, 32, 2, false, false>), grid_a, dim3(512), 0, stream, a);
+    }
   } else {
     hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.P0 + p.S, p.Hkv,
                        p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
-    if (pl.rows == 64)
-      hipLaunchKernelGGL((k_prefill4<256, 32, 64>), grid_a, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_prefill4<256, 32, 128>), grid_a, dim3(256), 0, stream, a);
+    if (a.span_end != nullptr) {
+      if (pl.rows == 64)
+        hipLaunchKernelGGL((k_prefill4<256, 32, 64, true>), grid_a, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_prefill4<256, 32, 128, true>), grid_a, dim3(256), 0, stream, a);
+    } else {
+      if (pl.rows == 64)
+        hipLaunchKernelGGL((k_prefill4<256, 32, 64, false>), grid_a, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_prefill4<256, 32, 128, false>), grid_a, dim3(256), 0, stream, a);
+    }
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   return hipGetLastError();

@@ -269,7 +269,15 @@ int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, in
  *              positions start_pos .. start_pos + seq_len - 1 and see cache
  *              rows 0 .. start_pos + seq_len - 1 (all written by the
  *              caller); 0 is a whole prompt
- *   span_end   reserved: must be NULL
+ *   span_end   NULL (causal), or device int32 [batch, seq_len]: for query s
+ *              the last position of its bidirectional span -- queries inside
+ *              a span of image tokens also see the span's later keys ([SG]
+ *              "Config note": bidirectional image attention) -- i.e. key j
+ *              passes the causal test iff j <= span_end[b][s]; outside
+ *              spans span_end[b][s] = start_pos + s.  Spans are disjoint
+ *              intervals inside the chunk: start_pos + s <= span_end[b][s] <
+ *              start_pos + seq_len (values outside are clamped into that
+ *              range).  The window test is unchanged.
  */
 typedef struct {
   int32_t start_pos;

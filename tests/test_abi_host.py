@@ -258,9 +258,9 @@ def test_compute_calls_reject_bad_arguments_without_gpu(lib):
     po = L.PrefillOpts(10, None)
     assert lib.gemma4_attn_prefill_ext(arr, n, 4, fake, tab, tab, 1, 16, 20, ctypes.byref(po), fake, fake, 1 << 20,
                                        None) == L.G4_ERR_INVALID_ARG
-    po = L.PrefillOpts(0, 0x10)
+    po = L.PrefillOpts(-1, None)
     assert lib.gemma4_attn_prefill_ext(arr, n, 4, fake, tab, tab, 1, 16, 20, ctypes.byref(po), fake, fake, 1 << 20,
-                                       None) == L.G4_ERR_UNSUPPORTED
+                                       None) == L.G4_ERR_INVALID_ARG
     do = L.DecodeOpts(5, None, None)
     assert lib.gemma4_attn_decode_ext(arr, n, 4, fake, tab, tab, fake, 4, 100, 4, ctypes.byref(do), fake, fake,
                                       1 << 30, None) == L.G4_ERR_INVALID_ARG

@@ -579,3 +579,46 @@ def test_decode_with_fused_append(B, T, Hq, Hkv, D, W, C, alias, kv_len, Lmax):
     assert np.array_equal(kd.cpu().view(torch.int16).numpy().view(np.uint16), kw), "key cache after the append"
     if vd is not None:
         assert np.array_equal(vd.cpu().view(torch.int16).numpy().view(np.uint16), vw), "value cache after the append"
+
+
+# ------------------------------------------------- bidirectional spans --
+# Queries inside a span (image tokens) also see the span's later keys.
+
+def _span_end(B, S, P0, spans_per_batch):
+    """int32 [B, S]: for query s (position P0 + s) the last position of its
+    span, or its own position; spans are inclusive (first, last) positions."""
+    e = np.tile(np.arange(P0, P0 + S, dtype=np.int32), (B, 1))
+    for b, spans in enumerate(spans_per_batch):
+        for a, z in spans:
+            e[b, a - P0:z - P0 + 1] = z
+    return e
+
+
+@pytest.mark.parametrize("B,S,P0,Hq,Hkv,D,W,alias,spans,override", [
+    (2, 600, 0, 8, 2, 512, 0, False, [[(50, 305), (400, 420)], [(0, 31), (100, 100), (570, 599)]], None),
+    (1, 300, 0, 8, 2, 512, 0, False, [[(10, 290)]], ("G4_PREFILL_SPLIT_PV", "0")),  # short segments, spans
+    (2, 700, 0, 8, 1, 256, 0, True, [[(64, 319)], [(5, 6), (200, 455)]], ("G4_PREFILL_ROWS", "64")),
+    (2, 700, 0, 8, 1, 256, 0, True, [[(64, 319)], [(5, 6), (200, 455)]], ("G4_PREFILL_ROWS", "128")),
+    (1, 500, 0, 8, 1, 256, 64, True, [[(100, 300)]], None),          # a span longer than the window
+    (1, 256, 900, 8, 2, 512, 0, False, [[(950, 1100)]], None),        # a chunk at a start position
+    (1, 1024, 0, 8, 1, 256, 0, False, [[(300, 900)]], ("G4_PREFILL_ROWS", "128")),  # tiles cut into pieces
+])
+def test_bidirectional_spans(monkeypatch, B, S, P0, Hq, Hkv, D, W, alias, spans, override):
+    import torch
+    if override:
+        monkeypatch.setenv(*override)
+    Lmax = P0 + S
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    q = inputs.normal_bf16([740, S, 0], (B, S, Hq, D))
+    k = inputs.normal_bf16([740, S, 1], (B, Hkv, Lmax, D))
+    v = None if alias else inputs.normal_bf16([740, S, 2], (B, Hkv, Lmax, D))
+    se = _span_end(B, S, P0, spans)
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias))])
+    ws = torch.full((st.prefill_workspace_bytes(0, B, S, P0),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    out = st.prefill(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)], workspace=ws, start_pos=P0,
+                     span_end=torch.from_numpy(se).to("cuda:0"))
+    torch.cuda.synchronize()
+    want = oracle.prefill(q, k, v, W, theta, start_pos=P0, span_end=se)
+    assert not np.array_equal(want, oracle.prefill(q, k, v, W, theta, start_pos=P0))  # the spans matter
+    check(out.cpu().numpy(), want, "spans B%d S%d P0=%d D%d W%d %s" % (B, S, P0, D, W, override))
