@@ -2059,7 +2059,10 @@ __device__ void decode_split(const DecodeArgs& a, long long& T, int& np, int& b_
 // recurrence).  The four waves split the rotation pairs for S^T = K' Q'^T
 // (partial sums exchanged through LDS) and the head dim for O^T += V^T P^T.
 // Key/value rows stream through NSTAGE LDS stages of 16 rows each.
-template <int D, bool ALIAS, int NSTAGE>
+// GEN = false is the one-token path over a cache of one row per position
+// with nothing appended (T = 1, ring = 0, knew = null): the per-column
+// positions, masks, ring rows and appended rows compile away.
+template <int D, bool ALIAS, int NSTAGE, bool GEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(DecodeArgs a) {
   constexpr int KPS = 16;            // keys per step
   constexpr int FQ = D / 8;          // rotation pairs per wave
@@ -2098,19 +2101,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   // MFMA column n is query column c = 16 cg + n of this (batch, kv head):
   // token t = c / g at position L - T + t, head kvh * g + c % g.
   const int c = cg * 16 + n;
-  const bool qvalid = n < a.cols && c < a.T * a.g;
-  const int ct = qvalid ? c / a.g : 0, hh = qvalid ? c % a.g : 0;
+  const bool qvalid = GEN ? (n < a.cols && c < a.T * a.g) : n < a.g;
+  const int ct = GEN && qvalid ? c / a.g : 0, hh = qvalid ? (GEN ? c % a.g : n) : 0;
   const int head = kvh * a.g + hh;
-  const int P = L - a.T + ct;  // this column's query position
+  const int P = GEN ? L - a.T + ct : L - 1;  // this column's query position
   const size_t part = (size_t)slot * a.cols + (qvalid ? n : 0);
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   // Keys of the T current tokens come from the appended rows when the call
   // writes them (k_decode_combine stores them into the cache afterwards).
-  const int new0 = a.knew != nullptr ? L - a.T : 0x7fffffff;
+  const int new0 = GEN && a.knew != nullptr ? L - a.T : 0x7fffffff;
   // Cache row of key position pos of this segment: row0 + (pos - k_start),
   // wrapped once for a ring (a segment spans at most the ring's length).
-  const int wrap = a.ring > 0 ? a.ring : 0x7fffffff;
-  const int row0 = a.ring > 0 ? k_start % a.ring : k_start;
+  const int wrap = GEN && a.ring > 0 ? a.ring : 0x7fffffff;
+  const int row0 = GEN && a.ring > 0 ? k_start % a.ring : k_start;
   auto issue = [&](int step, int stg) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -2125,9 +2128,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
         const int byte = blk * 1024 + ln * 16;
         const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
         const int pos = min(k0 + row, k_end - 1);  // key position
-        int crow = row0 + (pos - k_start);
-        crow = crow >= wrap ? crow - wrap : crow;
-        const uint16_t* src = pos >= new0 ? nbase + (size_t)(pos - new0) * a.Hkv * D : base + (size_t)crow * D;
+        const uint16_t* src;
+        if constexpr (GEN) {
+          int crow = row0 + (pos - k_start);
+          crow = crow >= wrap ? crow - wrap : crow;
+          src = pos >= new0 ? nbase + (size_t)(pos - new0) * a.Hkv * D : base + (size_t)crow * D;
+        } else {
+          src = base + (size_t)pos * D;
+        }
         g2l16_nt(src + ((slot ^ swz(row)) << 3), reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
       }
     }
@@ -2265,7 +2273,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int key = k0 + 4 * G + jj;
-      const bool vis = key < k_end && key <= P && (a.W == 0 || P - key < a.W);
+      const bool vis = GEN ? key < k_end && key <= P && (a.W == 0 || P - key < a.W) : key < k_end;
       sc[jj] = vis ? sc[jj] : kNegInf;
       mx = fmaxf(mx, sc[jj]);
     }
@@ -2701,16 +2709,18 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   fill_rope_rev(&a.rope, p.D, p.theta);
   const dim3 grid((unsigned)p.plan.npieces);
   if (ev.before) (void)hipEventRecord(ev.before, stream);
+  const bool gen = p.T > 1 || p.ring > 0 || p.k_new != nullptr;
+  auto run = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
   if (p.D == 512) {
     if (p.alias)
-      hipLaunchKernelGGL((k_decode<512, true, kDecodeStages>), grid, dim3(256), 0, stream, a);
+      gen ? run(k_decode<512, true, kDecodeStages, true>) : run(k_decode<512, true, kDecodeStages, false>);
     else
-      hipLaunchKernelGGL((k_decode<512, false, 2>), grid, dim3(256), 0, stream, a);
+      gen ? run(k_decode<512, false, 2, true>) : run(k_decode<512, false, 2, false>);
   } else {
     if (p.alias)
-      hipLaunchKernelGGL((k_decode<256, true, kDecodeStages>), grid, dim3(256), 0, stream, a);
+      gen ? run(k_decode<256, true, kDecodeStages, true>) : run(k_decode<256, true, kDecodeStages, false>);
     else
-      hipLaunchKernelGGL((k_decode<256, false, kDecodeStages>), grid, dim3(256), 0, stream, a);
+      gen ? run(k_decode<256, false, kDecodeStages, true>) : run(k_decode<256, false, kDecodeStages, false>);
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   // Streams of few pieces: one work-group per head; of many: 64-wide slices.
