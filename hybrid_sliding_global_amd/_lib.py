@@ -219,6 +219,11 @@ def _check_tensor(t, name, dtype, shape):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _cache_dtype(d):
+    import torch
+    return torch.uint8 if int(d.get("kv_dtype", 0)) == 1 else torch.bfloat16
+
+
 class Stack:
     """A stack of layer descriptors kept as a C array for repeated calls."""
 
@@ -269,9 +274,9 @@ class Stack:
             raise ValueError("k_caches[%d] is None" % src)
         Lmax = k.shape[2]
         _check_tensor(q, "q", torch.bfloat16, (B, S, d["num_q_heads"], d["head_dim"]))
-        _check_tensor(k, "k_cache", torch.bfloat16, (B, d["num_kv_heads"], Lmax, d["head_dim"]))
+        _check_tensor(k, "k_cache", _cache_dtype(d), (B, d["num_kv_heads"], Lmax, d["head_dim"]))
         if not d["kv_alias"]:
-            _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
+            _check_tensor(v_caches[src], "v_cache", _cache_dtype(d), tuple(k.shape))
         s = _resolve_stream(stream)
         if out is None:
             out = _alloc_on(s, (B, S, Hq, D), torch.float32, q.device)
@@ -315,9 +320,9 @@ class Stack:
         Lmax = k.shape[2]
         qshape = (B, T, d["num_q_heads"], d["head_dim"]) if multi else (B, d["num_q_heads"], d["head_dim"])
         _check_tensor(q, "q", torch.bfloat16, qshape)
-        _check_tensor(k, "k_cache", torch.bfloat16, (B, d["num_kv_heads"], Lmax, d["head_dim"]))
+        _check_tensor(k, "k_cache", _cache_dtype(d), (B, d["num_kv_heads"], Lmax, d["head_dim"]))
         if not d["kv_alias"]:
-            _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
+            _check_tensor(v_caches[src], "v_cache", _cache_dtype(d), tuple(k.shape))
         _check_tensor(kv_len, "kv_len", torch.int32, (B,))
         if k_new is not None:
             nshape = (B, T, d["num_kv_heads"], d["head_dim"]) if multi else (B, d["num_kv_heads"], d["head_dim"])
@@ -357,9 +362,9 @@ class Stack:
             raise ValueError("k_caches[%d] is None" % src)
         Lmax = k.shape[2]
         _check_tensor(q, "q", torch.bfloat16, (B, d["num_q_heads"], d["head_dim"]))
-        _check_tensor(k, "k_cache", torch.bfloat16, (B, d["num_kv_heads"], Lmax, d["head_dim"]))
+        _check_tensor(k, "k_cache", _cache_dtype(d), (B, d["num_kv_heads"], Lmax, d["head_dim"]))
         if not d["kv_alias"]:
-            _check_tensor(v_caches[src], "v_cache", torch.bfloat16, tuple(k.shape))
+            _check_tensor(v_caches[src], "v_cache", _cache_dtype(d), tuple(k.shape))
         _check_tensor(kv_len, "kv_len", torch.int32, (B,))
         _check_tensor(out, "out", torch.float32, (B, Hq, D))
         s = _resolve_stream(stream)

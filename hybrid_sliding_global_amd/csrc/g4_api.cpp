@@ -54,7 +54,11 @@ int check_desc(const g4_layer_desc& d, int idx) {
   if (!(d.rope_theta > 0.0) || !std::isfinite(d.rope_theta))
     return fail(G4_ERR_INVALID_ARG, "layer %d: rope_theta %g", idx, d.rope_theta);
   if (!(d.scale >= 0.f) || !std::isfinite(d.scale)) return fail(G4_ERR_INVALID_ARG, "layer %d: scale %g", idx, d.scale);
-  if (d.kv_dtype != G4_KV_BF16) return fail(G4_ERR_UNSUPPORTED, "layer %d: kv_dtype %d", idx, d.kv_dtype);
+  if (d.kv_dtype != G4_KV_BF16 && d.kv_dtype != G4_KV_FP8_E4M3)
+    return fail(G4_ERR_UNSUPPORTED, "layer %d: kv_dtype %d", idx, d.kv_dtype);
+  if (d.kv_dtype == G4_KV_FP8_E4M3 &&
+      (!(d.k_scale > 0.f) || !std::isfinite(d.k_scale) || !(d.v_scale > 0.f) || !std::isfinite(d.v_scale)))
+    return fail(G4_ERR_INVALID_ARG, "layer %d: E4M3 scales %g / %g", idx, d.k_scale, d.v_scale);
   if (d.kv_ring < 0) return fail(G4_ERR_INVALID_ARG, "layer %d: kv_ring %d", idx, d.kv_ring);
   if (d.kv_ring > 0 && (d.kind != G4_SLIDING || d.kv_ring < d.window))
     return fail(G4_ERR_INVALID_ARG, "layer %d: a ring cache (kv_ring %d) needs a sliding layer with window <= kv_ring",
@@ -85,6 +89,9 @@ int check_layer(const g4_layer_desc* layers, int32_t n_layers, int32_t idx) {
   if (src.kv_dtype != d.kv_dtype || src.kv_ring != d.kv_ring)
     return fail(G4_ERR_BAD_SOURCE, "layer %d: source layer %d has kv_dtype/kv_ring %d/%d, needs %d/%d", idx, s,
                 src.kv_dtype, src.kv_ring, d.kv_dtype, d.kv_ring);
+  if (d.kv_dtype == G4_KV_FP8_E4M3 && (src.k_scale != d.k_scale || src.v_scale != d.v_scale))
+    return fail(G4_ERR_BAD_SOURCE, "layer %d: source layer %d stores its cache with scales %g / %g, not %g / %g", idx,
+                s, src.k_scale, src.v_scale, d.k_scale, d.v_scale);
   return G4_OK;
 }
 
@@ -137,7 +144,8 @@ G4_EXPORT int gemma4_kv_bytes(const g4_layer_desc* layers, int32_t n_layers, int
     return ok();
   }
   const size_t rows = d.kv_ring > 0 ? (size_t)d.kv_ring : (size_t)max_len;  // a ring holds kv_ring rows
-  const size_t bytes = (size_t)batch * d.num_kv_heads * rows * d.head_dim * 2;
+  const size_t elem = d.kv_dtype == G4_KV_FP8_E4M3 ? 1 : 2;
+  const size_t bytes = (size_t)batch * d.num_kv_heads * rows * d.head_dim * elem;
   *k_bytes = bytes;
   *v_bytes = d.kv_alias ? 0 : bytes;
   return ok();
@@ -250,6 +258,9 @@ int prefill_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, c
   p.W = d.kind == G4_SLIDING ? d.window : 0;
   p.P0 = o.start_pos;
   p.span_end = o.span_end;
+  p.fp8 = d.kv_dtype == G4_KV_FP8_E4M3;
+  p.k_scale = p.fp8 ? d.k_scale : 1.f;
+  p.v_scale = p.fp8 ? (d.kv_alias ? d.k_scale : d.v_scale) : 1.f;
   p.scale = resolved_scale(d);
   p.theta = d.rope_theta;
   const hipError_t e = g4::launch_prefill(p, static_cast<hipStream_t>(stream), g_profile);
@@ -331,6 +342,9 @@ int decode_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, co
   p.alias = d.kv_alias;
   p.T = o.n_tokens;
   p.ring = d.kv_ring;
+  p.fp8 = d.kv_dtype == G4_KV_FP8_E4M3;
+  p.k_scale = p.fp8 ? d.k_scale : 1.f;
+  p.v_scale = p.fp8 ? (d.kv_alias ? d.k_scale : d.v_scale) : 1.f;
   p.k_new = o.k_new;
   p.v_new = d.kv_alias ? o.k_new : o.v_new;
   p.scale = resolved_scale(d);

@@ -52,6 +52,8 @@ struct PrefillLaunch {
   int B, S, Hq, Hkv, D, Lmax, W;
   int P0;             // position of query 0: queries P0 .. P0+S-1 over keys 0 .. P0+S-1
   const int32_t* span_end;  // null, or device [B, S]: last position of each query's bidirectional span
+  bool fp8;           // the cache holds E4M3 bytes: key element = code * k_scale, value = code * v_scale
+  float k_scale, v_scale;  // (v_scale is k_scale for an aliased layer; both 1 for bf16)
   float scale;        // softmax scale (already resolved, > 0)
   double theta;
 };
@@ -85,6 +87,8 @@ struct DecodeLaunch {
   int ring;             // 0: row j holds position j; C > 0: row j % C (Lmax == C)
   const void* k_new;    // null, or bf16 [B, T, Hkv, D]: keys of the T tokens, written into the cache
   const void* v_new;    // values of the T tokens (== k_new when aliased)
+  bool fp8;             // the cache holds E4M3 bytes: key element = code * k_scale, value = code * v_scale
+  float k_scale, v_scale;
   float scale;
   double theta;
   DecodePlan plan;

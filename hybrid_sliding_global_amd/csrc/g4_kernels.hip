@@ -79,6 +79,22 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+// Eight E4M3 bytes (OCP encoding, what gfx950's conversions read) -> eight
+// packed bf16: exact, since every E4M3 value is a bf16 value.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    r[2 * i] = pack_bf16(lo[0], lo[1]);
+    r[2 * i + 1] = pack_bf16(hi[0], hi[1]);
+  }
+  return r;
+}
+
 // sin/cos of 2*pi*(pos*rev): the product and its reduction to [-1/2, 1/2]
 // revolutions are exact enough in fp64 for positions up to 2^31; the
 // hardware sin/cos (input in revolutions) then runs on a small argument.
@@ -156,8 +172,6 @@ __device__ __forceinline__ void lds_read_b128x4(u32x4 (&r)[4], const unsigned (&
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
 }
-
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 // Eight transpose reads (ds_read_b64_tr_b16): lane i of each 16-lane group
 // receives column (i % 4) of the 4x16-bit rows addressed by lanes
@@ -286,11 +300,21 @@ __device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsi
 // ones its value image.  Every thread issues all of its global loads before
 // it uses any of them, so a work-group costs one memory round trip rather
 // than one per loop step.
-template <int D, int BN>
-__global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+// FP8: the cache holds E4M3 bytes; their codes are imaged exactly (the
+// scales are applied to the queries and to the output instead).
+template <int D, int BN, bool FP8>
+__global__ __launch_bounds__(256) void k_prefill_prep(const void* __restrict__ k, const void* __restrict__ v,
                                                       uint16_t* __restrict__ kimg, uint16_t* __restrict__ vimg,
                                                       int nkeys, int Hkv, int Lmax, int ntiles, RopeRev rope,
                                                       int* counters, int ncounters) {
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per cache element
+  // 8 consecutive elements of a cache row, as packed bf16
+  auto load8 = [](const char* p) -> u32x4 {
+    if constexpr (FP8)
+      return fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(p));
+    else
+      return *reinterpret_cast<const u32x4*>(p);
+  };
   constexpr int KSTEPS = D / 16, DB = D / 32, KV = BN / 16;
   constexpr int PITCH = D + 8;  // staged value row, bf16 elements (16-byte skew per row)
   constexpr int CH = D / 16;    // 16-byte chunks per half key row
@@ -300,23 +324,23 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict
   const int t = blockIdx.x >> 1, kvh = blockIdx.y, b = blockIdx.z;
   const int flat = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
   for (int i = flat * 256 + threadIdx.x; i < ncounters; i += gridDim.x * gridDim.y * gridDim.z * 256) counters[i] = 0;
-  const size_t slice = ((size_t)b * Hkv + kvh) * (size_t)Lmax * D;
+  const size_t slice = ((size_t)b * Hkv + kvh) * (size_t)Lmax * D * EB;  // bytes
   const size_t tile = (((size_t)b * Hkv + kvh) * ntiles + t) * (size_t)(BN * D);
 
   if ((blockIdx.x & 1) == 0) {
     // keys: chunk c (8 elements at 8c) of the first half pairs with chunk c of
     // the second half; a thread keeps one chunk index c for all its rows
     static_assert(256 % CH == 0, "chunk index fixed per thread");
-    const uint16_t* ksrc = k + slice;
+    const char* ksrc = static_cast<const char*>(k) + slice;
     uint16_t* kdst = kimg + tile;
     const int c = threadIdx.x % CH, row0 = threadIdx.x / CH;
     u32x4 x[NK], y[NK];
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int p = t * BN + row0 + j * (256 / CH);
-      const uint16_t* r = ksrc + (size_t)min(p, nkeys - 1) * D;  // rows past the keys load the last, then become zeros
-      x[j] = *reinterpret_cast<const u32x4*>(r + 8 * c);
-      y[j] = *reinterpret_cast<const u32x4*>(r + D / 2 + 8 * c);
+      const char* r = ksrc + (size_t)min(p, nkeys - 1) * D * EB;  // rows past the keys load the last, then become zeros
+      x[j] = load8(r + 8 * c * EB);
+      y[j] = load8(r + (D / 2 + 8 * c) * EB);
     }
     double rev[8];
 #pragma unroll
@@ -337,13 +361,13 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const uint16_t* __restrict
   }
 
   // values: stage the tile's rows, then gather the transposed lane slots
-  const uint16_t* vsrc = v + slice;
+  const char* vsrc = static_cast<const char*>(v) + slice;
   uint16_t* vdst = vimg + tile;
   u32x4 x[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int it = threadIdx.x + 256 * j, row = it / (D / 8), c = it % (D / 8), p = t * BN + row;
-    x[j] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)min(p, nkeys - 1) * D + 8 * c);
+    x[j] = load8(vsrc + ((size_t)min(p, nkeys - 1) * D + 8 * c) * EB);
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -379,7 +403,8 @@ struct PrefillArgs {
   int P0;      // position of query 0 (keys 0 .. P0 + S - 1 are visible to the chunk)
   const int32_t* span_end;  // null (causal), or [B, S]: the last position of each query's bidirectional span
   int paired;  // 1: work unit = query tiles t and nqt-1-t; 0: one query tile
-  float qscale;  // softmax scale * log2(e): scores come out in log2 units
+  float qscale;  // softmax scale * log2(e) (times the key scale of an E4M3 cache): scores in log2 units
+  float vscale;  // the value scale of an E4M3 cache (1 otherwise): multiplies every output
   RopeRev rope;
 };
 
@@ -1073,7 +1098,7 @@ k_prefill(PrefillArgs a) {
     }
 
     const float l = l_i + __shfl_xor(l_i, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? a.vscale / l : 0.f;
     // (the row's coordinates are recomputed here rather than kept live
     // through the tile loop, where every register is taken)
     const int r_o = __builtin_amdgcn_readfirstlane(r0) + rg * 32 + n;
@@ -1751,7 +1776,7 @@ k_prefill4(PrefillArgs a) {
               lsum = k == 0 ? lp[0][rb] * f[0][rb] : __builtin_fmaf(lp[k][rb], f[k][rb], lsum);
             }
             const float lt = lsum + __shfl_xor(lsum, 32);
-            inv[rb] = lt > 0.f ? 1.f / lt : 0.f;
+            inv[rb] = lt > 0.f ? a.vscale / lt : 0.f;
           }
         }
         constexpr int NG = RB * DBW * 2;
@@ -1838,7 +1863,7 @@ k_prefill4(PrefillArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const float lt = lsum[rb] + __shfl_xor(lsum[rb], 32);
-          const float inv = lt > 0.f ? 1.f / lt : 0.f;
+          const float inv = lt > 0.f ? a.vscale / lt : 0.f;
           float* orow = out_row(rb);
           if (orow) {
 #pragma unroll
@@ -1869,7 +1894,7 @@ k_prefill4(PrefillArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = R64 ? sl[32 * rb + n] : sl[rb * 64 + lane];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? a.vscale / lt : 0.f;
       float* orow = out_row(rb);
       if (orow) {
 #pragma unroll
@@ -1912,7 +1937,9 @@ struct DecodeArgs {
   const uint16_t* vnew;  // their values (== knew when aliased)
   uint16_t* kc;          // the cache, written by k_decode_combine when appending
   uint16_t* vc;
-  float qscale;
+  float qscale;          // softmax scale * log2(e) (times the key scale of an E4M3 cache)
+  float vscale;          // the value scale of an E4M3 cache (1 otherwise): multiplies the output
+  float kstore, vstore;  // E4M3 append: the scales new keys / values are divided by
   RopeRev rope;
 };
 
@@ -1936,6 +1963,15 @@ __device__ __forceinline__ void lds_read_b128x2(u32x4 (&r)[2], const unsigned (&
   asm volatile(
       "ds_read_b128 %0, %2\n\t"
       "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(ad[0]), "v"(ad[1]));
+}
+
+__device__ __forceinline__ void lds_read_b64x2(u32x2 (&r)[2], const unsigned (&ad)[2]) {
+  asm volatile(
+      "ds_read_b64 %0, %2\n\t"
+      "ds_read_b64 %1, %3\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1])
       : "v"(ad[0]), "v"(ad[1]));
@@ -2061,8 +2097,12 @@ __device__ void decode_split(const DecodeArgs& a, long long& T, int& np, int& b_
 // Key/value rows stream through NSTAGE LDS stages of 16 rows each.
 // GEN = false is the one-token path over a cache of one row per position
 // with nothing appended (T = 1, ring = 0, knew = null): the per-column
-// positions, masks, ring rows and appended rows compile away.
-template <int D, bool ALIAS, int NSTAGE, bool GEN>
+// positions, masks, ring rows and appended rows compile away.  FP8: the
+// cache holds E4M3 bytes; a lane converts its key elements in registers
+// before rotating them, and each stage's values are converted once into a
+// bf16 tile laid out like a bf16 stage, which the value reads then use (the
+// key scale is in qscale, the value scale in the output).
+template <int D, bool ALIAS, int NSTAGE, bool GEN, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(DecodeArgs a) {
   constexpr int KPS = 16;            // keys per step
   constexpr int FQ = D / 8;          // rotation pairs per wave
@@ -2071,12 +2111,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   constexpr int DQ = D / 4;          // output head-dim slice per wave
   constexpr int DBLK = DQ / 16;
   constexpr int NT = ALIAS ? 1 : 2;  // tensors staged per step
-  constexpr int ROWB = D * 2;
+  constexpr int EB = FP8 ? 1 : 2;    // bytes per cache element
+  constexpr int ROWB = D * EB;       // bytes per staged cache row
+  constexpr int VROWB = D * 2;       // bytes per bf16 value row read by the output MFMAs
   constexpr int LPS1 = KPS * ROWB / 4096;
   constexpr int LPS = NT * LPS1;
   static_assert(LPS1 >= 1 && LPS1 * 4096 == KPS * ROWB, "stage must split over 256 threads");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[NSTAGE][NT][KPS * D];
+  __shared__ __attribute__((aligned(16))) unsigned char sbuf[NSTAGE][NT][KPS * ROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char vconv[FP8 ? KPS * VROWB : 16];
   __shared__ f32x4 red[4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, G = lane >> 4;
@@ -2109,7 +2152,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   // Keys of the T current tokens come from the appended rows when the call
   // writes them (k_decode_combine stores them into the cache afterwards).
-  const int new0 = GEN && a.knew != nullptr ? L - a.T : 0x7fffffff;
+  const int new0 = GEN && !FP8 && a.knew != nullptr ? L - a.T : 0x7fffffff;
   // Cache row of key position pos of this segment: row0 + (pos - k_start),
   // wrapped once for a ring (a segment spans at most the ring's length).
   const int wrap = GEN && a.ring > 0 ? a.ring : 0x7fffffff;
@@ -2120,23 +2163,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
     const int k0 = k_start + step * KPS;
 #pragma unroll
     for (int tsr = 0; tsr < NT; ++tsr) {
-      const uint16_t* base = (tsr == 0 ? a.k : a.v) + slice;
-      const uint16_t* nbase = (tsr == 0 ? a.knew : a.vnew) + ((size_t)b * a.T * a.Hkv + kvh) * D;
+      const char* base = reinterpret_cast<const char*>(tsr == 0 ? a.k : a.v) + slice * EB;
+      const char* nbase =
+          reinterpret_cast<const char*>((tsr == 0 ? a.knew : a.vnew) + ((size_t)b * a.T * a.Hkv + kvh) * D);
 #pragma unroll
       for (int i = 0; i < LPS1; ++i) {
         const int blk = i * 4 + wave;
         const int byte = blk * 1024 + ln * 16;
         const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
         const int pos = min(k0 + row, k_end - 1);  // key position
-        const uint16_t* src;
+        const char* src;
         if constexpr (GEN) {
           int crow = row0 + (pos - k_start);
           crow = crow >= wrap ? crow - wrap : crow;
-          src = pos >= new0 ? nbase + (size_t)(pos - new0) * a.Hkv * D : base + (size_t)crow * D;
+          // (appended rows are bf16 and read here only for a bf16 cache; an
+          // E4M3 cache has them quantised and stored before this kernel)
+          src = pos >= new0 ? nbase + (size_t)(pos - new0) * a.Hkv * D * 2 : base + (size_t)crow * ROWB;
         } else {
-          src = base + (size_t)pos * D;
+          src = base + (size_t)pos * ROWB;
         }
-        g2l16_nt(src + ((slot ^ swz(row)) << 3), reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
+        g2l16_nt(src + ((slot ^ swz(row)) << 4), reinterpret_cast<char*>(sbuf[stg][tsr]) + blk * 1024);
       }
     }
   };
@@ -2233,6 +2279,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
       wait_vm<0>();
     lds_barrier();
     if (s + NSTAGE - 1 < nsteps) issue(s + NSTAGE - 1, (s + NSTAGE - 1) % NSTAGE);
+    if constexpr (FP8) {
+      // This stage's values (the keys of an aliased layer) as bf16 rows in
+      // the bf16 stage layout: E4M3 chunk cf (16 elements) of row r sits at
+      // 16-byte slot cf ^ swz(r); its halves are bf16 chunks 2 cf and
+      // 2 cf + 1, stored at slots (2 cf) ^ swz(r) and (2 cf + 1) ^ swz(r).
+      // Written before, and read after, the score-exchange barrier below.
+      const unsigned char* vs8 = sbuf[stg][NT - 1];
+#pragma unroll
+      for (int i = 0; i < D / 256; ++i) {
+        const int ci = tid + 256 * i, r = ci / (D / 16), cf = ci % (D / 16);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(vs8 + r * ROWB + ((cf ^ swz(r)) << 4));
+        unsigned char* vrow = vconv + r * VROWB;
+        *reinterpret_cast<u32x4*>(vrow + (((2 * cf) ^ swz(r)) << 4)) = fp8x8_to_bf16(u32x2{w[0], w[1]});
+        *reinterpret_cast<u32x4*>(vrow + (((2 * cf + 1) ^ swz(r)) << 4)) = fp8x8_to_bf16(u32x2{w[2], w[3]});
+      }
+    }
 
     int ln = lane;  // opaque lane index: per-lane LDS offsets are recomputed each step
     asm volatile("" : "+v"(ln));
@@ -2247,9 +2309,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int d = wave * FQ + 32 * kk + 8 * oG;
-      const unsigned ad[2] = {kra + (((d >> 3) ^ ksw) << 4), kra + ((((d + D / 2) >> 3) ^ ksw) << 4)};
       u32x4 fr[2];
-      lds_read_b128x2(fr, ad);
+      if constexpr (FP8) {
+        // 8 E4M3 bytes at element d (16-byte chunk d / 16, half (d / 8) & 1)
+        const unsigned ad[2] = {kra + (((d >> 4) ^ ksw) << 4) + (d & 8),
+                                kra + ((((d + D / 2) >> 4) ^ ksw) << 4) + ((d + D / 2) & 8)};
+        u32x2 f8[2];
+        lds_read_b64x2(f8, ad);
+        fr[0] = fp8x8_to_bf16(f8[0]);
+        fr[1] = fp8x8_to_bf16(f8[1]);
+      } else {
+        const unsigned ad[2] = {kra + (((d >> 3) ^ ksw) << 4), kra + ((((d + D / 2) >> 3) ^ ksw) << 4)};
+        lds_read_b128x2(fr, ad);
+      }
       rot8_const(fr[0], fr[1], kcs[kk]);
       sp = mfma16(as_bf16x8(fr[0]), qf[kk], sp);
       sp = mfma16(as_bf16x8(fr[1]), qf[kk + KH], sp);
@@ -2297,9 +2369,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
 
     // O^T += V^T P^T with 16x16x16 MFMAs: P^T slot t of lane group G is key
     // 4*G + t, which one transpose read per output block fetches.
-    const char* vb = reinterpret_cast<const char*>(sbuf[stg][NT - 1]);
+    const char* vb = FP8 ? reinterpret_cast<const char*>(vconv) : reinterpret_cast<const char*>(sbuf[stg][NT - 1]);
     const int vrow = 4 * oG + (on >> 2);
-    const unsigned va = lds_addr(vb + vrow * ROWB);
+    const unsigned va = lds_addr(vb + vrow * VROWB);
     const int vsw = swz(vrow);
 #pragma unroll
     for (int b0 = 0; b0 < DBLK; b0 += 4) {
@@ -2319,7 +2391,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   // (a column can see no key of a segment: with T > 1 the keys after its
   // position, or before its window; its partial is then 0 with weight 0)
   const float l = sum_over_groups(l_i);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l > 0.f ? a.vscale / l : 0.f;
   if (qvalid) {
     float* o = a.part_o + part * D + wave * DQ + 4 * G;
 #pragma unroll
@@ -2344,6 +2416,44 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
                 (b * a.Hkv) * a.ncg + st + piece);
     }
     base += (long long)a.Hkv * a.ncg * span;
+  }
+}
+
+// Append to an E4M3 cache: the T tokens' keys (and values) of one (batch,
+// token, kv head) per work-group, stored as E4M3 codes of x / scale (the
+// quotient in fp32, rounded to nearest with ties to even by the hardware
+// conversion, clamped to +-448 first so that it saturates) into their rows.
+// Runs before the split-K kernel, which then reads them from the cache.
+template <int D>
+__global__ __launch_bounds__(64) void k_append_fp8(DecodeArgs a) {
+  const int kvh = blockIdx.x % a.Hkv, bt = blockIdx.x / a.Hkv, tok = bt % a.T, b = bt / a.T;
+  const int P = decode_len(a, b) - a.T + tok;
+  const size_t dst = ((size_t)(b * a.Hkv + kvh) * a.Lmax + decode_row(a, P)) * D;  // E4M3 bytes
+  const size_t src = (((size_t)b * a.T + tok) * a.Hkv + kvh) * D;                   // bf16 elements
+  auto quant8 = [](const uint16_t* x, float scale) -> u32x2 {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(x);
+    u32x2 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned wv = w[2 * i + e / 2];
+        const float f = (e & 1) ? bf_hi(wv) : bf_lo(wv);
+        q[e] = fminf(fmaxf(f / scale, -448.f), 448.f);
+      }
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], pk, true);
+      r[i] = (unsigned)pk;
+    }
+    return r;
+  };
+  for (int i = threadIdx.x; i < D / 8; i += 64) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(a.kc) + dst + 8 * i) = quant8(a.knew + src + 8 * i,
+                                                                                             a.kstore);
+    if (a.vnew != a.knew)
+      *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(a.vc) + dst + 8 * i) =
+          quant8(a.vnew + src + 8 * i, a.vstore);
   }
 }
 
@@ -2614,17 +2724,22 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   a.npair = pl.npair;
   a.paired = pl.paired;
   a.kpieces = pl.kpieces;
-  a.qscale = p.scale * kLog2e;
+  a.qscale = p.scale * kLog2e * p.k_scale;
+  a.vscale = p.v_scale;
   fill_rope_rev(&a.rope, p.D, p.theta);
   const dim3 grid_k(2 * pl.ntiles, p.Hkv, p.B);
   const dim3 grid_a((unsigned)((long)p.B * p.Hkv * pl.npair * pl.kpieces));
-  const uint16_t* kraw = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vraw = static_cast<const uint16_t*>(p.v);
+  const void* kraw = p.k;
+  const void* vraw = p.v;
   uint16_t* kimg = reinterpret_cast<uint16_t*>(ws);
   uint16_t* vimg = reinterpret_cast<uint16_t*>(ws + pl.vimg_off);
   if (p.D == 512) {
-    hipLaunchKernelGGL((k_prefill_prep<512, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.P0 + p.S, p.Hkv,
-                       p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+    if (p.fp8)
+      hipLaunchKernelGGL((k_prefill_prep<512, 32, true>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
+                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+    else
+      hipLaunchKernelGGL((k_prefill_prep<512, 32, false>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
+                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     if (a.span_end != nullptr) {
       // (spans run the split-PV schedule at every length: the other one's
@@ -2637,8 +2752,12 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
         hipLaunchKernelGGL((k_prefill<512, 32, 2, false, false>), grid_a, dim3(512), 0, stream, a);
     }
   } else {
-    hipLaunchKernelGGL((k_prefill_prep<256, 32>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg, p.P0 + p.S, p.Hkv,
-                       p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+    if (p.fp8)
+      hipLaunchKernelGGL((k_prefill_prep<256, 32, true>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
+                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+    else
+      hipLaunchKernelGGL((k_prefill_prep<256, 32, false>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
+                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     if (a.span_end != nullptr) {
       if (pl.rows == 64)
@@ -2705,22 +2824,47 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   a.Lmax = p.Lmax;
   a.W = p.W;
   a.npieces = p.plan.npieces;
-  a.qscale = p.scale * kLog2e;
+  a.qscale = p.scale * kLog2e * p.k_scale;
+  a.vscale = p.v_scale;
+  a.kstore = p.k_scale;
+  a.vstore = p.alias ? p.k_scale : p.v_scale;
   fill_rope_rev(&a.rope, p.D, p.theta);
   const dim3 grid((unsigned)p.plan.npieces);
+  if (p.fp8 && a.knew != nullptr) {
+    // an E4M3 cache takes the new rows quantised before the attention reads it
+    const dim3 ga((unsigned)(p.B * p.T * p.Hkv));
+    if (p.D == 512)
+      hipLaunchKernelGGL((k_append_fp8<512>), ga, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_append_fp8<256>), ga, dim3(64), 0, stream, a);
+    a.knew = a.vnew = nullptr;
+  }
   if (ev.before) (void)hipEventRecord(ev.before, stream);
-  const bool gen = p.T > 1 || p.ring > 0 || p.k_new != nullptr;
+  const bool gen = p.T > 1 || p.ring > 0 || a.knew != nullptr;
   auto run = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
+  // LDS stages: 4 of 16 rows, except head size 512 with separate K and V
+  // (2 of bf16, 3 of E4M3 beside the converted value tile), so that two
+  // work-groups share a CU
+  auto pick = [&](auto d_c, auto alias_c, auto fp8_c) {
+    constexpr int D = decltype(d_c)::value;
+    constexpr bool AL = decltype(alias_c)::value, F8 = decltype(fp8_c)::value;
+    constexpr int NS = (D == 512 && !AL) ? (F8 ? 3 : 2) : kDecodeStages;
+    gen ? run(k_decode<D, AL, NS, true, F8>) : run(k_decode<D, AL, NS, false, F8>);
+  };
+  using D512 = std::integral_constant<int, 512>;
+  using D256 = std::integral_constant<int, 256>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (p.D == 512) {
     if (p.alias)
-      gen ? run(k_decode<512, true, kDecodeStages, true>) : run(k_decode<512, true, kDecodeStages, false>);
+      p.fp8 ? pick(D512{}, T_{}, T_{}) : pick(D512{}, T_{}, F_{});
     else
-      gen ? run(k_decode<512, false, 2, true>) : run(k_decode<512, false, 2, false>);
+      p.fp8 ? pick(D512{}, F_{}, T_{}) : pick(D512{}, F_{}, F_{});
   } else {
     if (p.alias)
-      gen ? run(k_decode<256, true, kDecodeStages, true>) : run(k_decode<256, true, kDecodeStages, false>);
+      p.fp8 ? pick(D256{}, T_{}, T_{}) : pick(D256{}, T_{}, F_{});
     else
-      gen ? run(k_decode<256, false, kDecodeStages, true>) : run(k_decode<256, false, kDecodeStages, false>);
+      p.fp8 ? pick(D256{}, F_{}, T_{}) : pick(D256{}, F_{}, F_{});
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);
   // Streams of few pieces: one work-group per head; of many: 64-wide slices.

@@ -46,6 +46,19 @@ def normal_bf16(seed: Sequence[int], shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+NAN_E4M3 = np.uint8(0x7F)
+
+
+def normal_e4m3(seed: Sequence[int], shape, scale: float) -> np.ndarray:
+    """E4M3 bytes (OCP encoding) of N(0,1) samples divided by ``scale`` (torch's
+    round-to-nearest conversion): an 8-bit cache whose elements times
+    ``scale`` are about N(0,1)."""
+    import torch
+    rng = np.random.default_rng(list(seed))
+    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32) / np.float32(scale)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(shape)
+
+
 def zeros_bf16(shape) -> np.ndarray:
     return np.zeros(shape, np.uint16)
 
@@ -57,13 +70,15 @@ def kv_lengths_uniform(seed: Sequence[int], batch: int, lo: int, hi: int) -> np.
 
 
 def poison_beyond(cache: np.ndarray, kv_len: np.ndarray) -> np.ndarray:
-    """Fill cache rows at or beyond each sequence's length with bfloat16 NaN.
+    """Fill cache rows at or beyond each sequence's length with NaN (bfloat16
+    or E4M3, by the array's dtype).
 
     ``cache`` is [B, H, Lmax, D]; a kernel that reads a row it must not read
     then produces NaN in its output.
     """
+    nan = NAN_E4M3 if cache.dtype == np.uint8 else NAN_BF16
     for b, L in enumerate(np.asarray(kv_len)):
-        cache[b, :, int(L):, :] = NAN_BF16
+        cache[b, :, int(L):, :] = nan
     return cache
 
 

@@ -110,17 +110,22 @@ extern "C" {
  *                   "Gemma 4 Model Details" (separate theta values for
  *                   sliding and full attention); [LD] module comment (dual
  *                   RoPE theta).
- *   kv_dtype        element type of the layer's cache: G4_KV_BF16 (0) --
- *                   [LD] load_layers (layer_kv_dtypes: a KV cache dtype per
- *                   layer).  Must equal the source layer's.
+ *   kv_dtype        element type of the layer's cache: G4_KV_BF16 (0) or
+ *                   G4_KV_FP8_E4M3 (1, one byte per element in the OCP E4M3
+ *                   encoding: the element's value is code * k_scale for keys,
+ *                   code * v_scale for values) -- [LD] load_layers
+ *                   (layer_kv_dtypes: a KV cache dtype per layer).  Must
+ *                   equal the source layer's.
  *   kv_ring         0: the cache holds row j for position j ([batch, Hkv,
  *                   max_len, head_dim]); C > 0: a window-sized ring of C rows
  *                   per (batch, kv head), position j in row j mod C (sliding
  *                   layers only, C >= window; decode only) -- [FR] "What
  *                   Would Need to Change" item 2 (variable-size KV cache
  *                   buffers per layer).  Must equal the source layer's.
- *   k_scale,        reserved for 8-bit caches; ignored for G4_KV_BF16.
- *   v_scale
+ *   k_scale,        G4_KV_FP8_E4M3: the per-tensor scales of the cached
+ *   v_scale         keys and values (> 0; an aliased layer's values use
+ *                   k_scale); a shared layer must give its source's.  Ignored
+ *                   for G4_KV_BF16 -- [LD] load_layers (layer_kv_dtypes).
  */
 typedef struct {
   int32_t kind;
@@ -140,6 +145,7 @@ typedef struct {
 
 /* Cache element types (kv_dtype). */
 #define G4_KV_BF16 0
+#define G4_KV_FP8_E4M3 1
 
 /* ABI version of the loaded library (G4_ABI_VERSION at build time).  Library
  * plumbing; no passage of the pages defines it. */
@@ -296,7 +302,10 @@ typedef struct {
  *              (row of position kv_len[b] - T + t, modulo kv_ring for a
  *              ring) and attends to them as if they had been there -- the
  *              fused append a window-sized cache needs ([FR] "What Would
- *              Need to Change" item 2)
+ *              Need to Change" item 2).  An E4M3 cache stores the code of
+ *              x / scale (binary32 quotient, nearest E4M3 value with ties to
+ *              even, saturating at +-448) and the attention reads those
+ *              codes back
  *   v_new      likewise the values; NULL for an aliased layer (the keys are
  *              the values), required otherwise when k_new is given
  */

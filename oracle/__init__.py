@@ -92,6 +92,8 @@ def _load():
         lib.orc_decode_ext.restype = ctypes.c_int
         lib.orc_fp8_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         lib.orc_fp8_e4m3_to_f64.restype = ctypes.c_double
+        lib.orc_fp8_e4m3_quantize.argtypes = [ctypes.c_float, ctypes.c_float]
+        lib.orc_fp8_e4m3_quantize.restype = ctypes.c_uint8
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -174,6 +176,15 @@ def fp8_e4m3_value(codes) -> np.ndarray:
     lib = _load()
     c = np.asarray(codes, np.uint8)
     return np.array([lib.orc_fp8_e4m3_to_f64(int(x)) for x in c.ravel()], np.float64).reshape(c.shape)
+
+
+def fp8_e4m3_quantize(x, scale: float) -> np.ndarray:
+    """E4M3 codes of x / scale (quotient in float32, nearest value, ties to
+    even, saturating at +-448): what an 8-bit cache stores for the values x."""
+    lib = _load()
+    a = np.asarray(x, np.float32)
+    return np.array([lib.orc_fp8_e4m3_quantize(float(v), float(scale)) for v in a.ravel()],
+                    np.uint8).reshape(a.shape)
 
 
 def _kv(a: Optional[np.ndarray]):

@@ -90,6 +90,26 @@ double orc_fp8_e4m3_to_f64(uint8_t b) {
   return s ? -v : v;
 }
 
+/* E4M3 code of x / scale, the element an 8-bit cache stores for the value x:
+ * the quotient is taken in binary32 (the precision the library computes it
+ * in), then rounded to the nearest E4M3 value (ties to the even code, i.e.
+ * mantissa LSB 0); magnitudes beyond the largest finite value 448 saturate
+ * to +-448.  Found by scanning the 127 finite non-negative codes. */
+uint8_t orc_fp8_e4m3_quantize(float x, float scale) {
+  const float qf = x / scale;
+  const double q = (double)qf;
+  const int neg = signbit(qf) ? 1 : 0;
+  const double a = fabs(q);
+  if (isnan(q)) return 0x7F;
+  int best = 0;
+  for (int c = 1; c < 127; ++c) {
+    const double dc = fabs(orc_fp8_e4m3_to_f64((uint8_t)c) - a);
+    const double db = fabs(orc_fp8_e4m3_to_f64((uint8_t)best) - a);
+    if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)(best | (neg << 7));
+}
+
 /* RoPE inverse frequencies theta^(-2k/D), k = 0 .. D/2-1 (dual theta: the
  * caller passes the layer's own theta). */
 void orc_rope_inv_freq(int32_t D, double theta, double* out) {

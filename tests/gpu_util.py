@@ -22,8 +22,10 @@ REL_RMS = 1e-2
 
 
 def to_dev(a: np.ndarray):
-    """uint16 bfloat16 bits -> torch bf16 tensor on cuda:0."""
+    """uint16 bfloat16 bits -> torch bf16 tensor on cuda:0 (uint8 E4M3 bytes stay uint8)."""
     import torch
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 

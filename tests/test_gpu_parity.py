@@ -622,3 +622,106 @@ def test_bidirectional_spans(monkeypatch, B, S, P0, Hq, Hkv, D, W, alias, spans,
     want = oracle.prefill(q, k, v, W, theta, start_pos=P0, span_end=se)
     assert not np.array_equal(want, oracle.prefill(q, k, v, W, theta, start_pos=P0))  # the spans matter
     check(out.cpu().numpy(), want, "spans B%d S%d P0=%d D%d W%d %s" % (B, S, P0, D, W, override))
+
+
+# ----------------------------------------------------- 8-bit KV caches --
+# A layer's cache may hold E4M3 bytes with one scale per tensor: element =
+# code * k_scale (keys) or code * v_scale (values; k_scale when aliased).
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,W,alias,ks,vs,override", [
+    (1, 640, 8, 2, 512, 0, False, 0.3, 1.7, ("G4_PREFILL_SPLIT_PV", "0")),
+    (1, 640, 8, 2, 512, 0, False, 0.3, 1.7, ("G4_PREFILL_SPLIT_PV", "1")),
+    (2, 333, 8, 1, 256, 48, True, 0.125, 1.0, ("G4_PREFILL_ROWS", "64")),
+    (2, 333, 8, 1, 256, 48, True, 0.125, 1.0, ("G4_PREFILL_ROWS", "128")),
+    (1, 1000, 8, 1, 256, 512, False, 0.07, 0.4, None),
+])
+def test_fp8_cache_prefill(monkeypatch, B, S, Hq, Hkv, D, W, alias, ks, vs, override):
+    import torch
+    if override:
+        monkeypatch.setenv(*override)
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    q = inputs.normal_bf16([750, S, 0], (B, S, Hq, D))
+    k = inputs.normal_e4m3([750, S, 1], (B, Hkv, S + 3, D), ks)
+    v = None if alias else inputs.normal_e4m3([750, S, 2], (B, Hkv, S + 3, D), vs)
+    k[:, :, S:] = inputs.NAN_E4M3
+    if v is not None:
+        v[:, :, S:] = inputs.NAN_E4M3
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias), kv_dtype=wl.KV_FP8, k_scale=ks, v_scale=vs)])
+    out = st.prefill(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)])
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), oracle.prefill(q, k, v, W, theta, k_scale=ks, v_scale=vs),
+          "fp8 prefill D%d W%d alias%d %s" % (D, W, alias, override))
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,W,alias,ring,kv_len,ks,vs", [
+    (4, 1, 8, 2, 512, 0, False, 0, [1, 33, 1000, 4096], 0.3, 1.7),     # three 16-row stages beside the value tile
+    (3, 1, 8, 2, 512, 0, True, 0, [700, 2, 3000], 0.5, 0.5),
+    (4, 1, 8, 1, 256, 1024, True, 0, [1, 500, 1025, 3000], 0.125, 0.125),
+    (3, 1, 16, 2, 256, 0, False, 0, [64, 65, 2000], 0.2, 3.0),
+    (2, 3, 8, 2, 512, 0, False, 0, [5000, 3], 0.3, 1.7),               # multi-token
+    (3, 1, 8, 1, 256, 1024, True, 1024, [5000, 1024, 17], 0.25, 0.25),  # ring
+])
+def test_fp8_cache_decode(B, T, Hq, Hkv, D, W, alias, ring, kv_len, ks, vs):
+    import torch
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    kv = np.asarray(kv_len, np.int32)
+    rows = ring if ring else int(kv.max())
+    q = inputs.normal_bf16([760, T, 0], (B, T, Hq, D) if T > 1 else (B, Hq, D))
+    k = inputs.normal_e4m3([760, T, 1], (B, Hkv, rows, D), ks)
+    v = None if alias else inputs.normal_e4m3([760, T, 2], (B, Hkv, rows, D), vs)
+    if not ring:
+        inputs.poison_beyond(k, kv)
+        if v is not None:
+            inputs.poison_beyond(v, kv)
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias), kv_dtype=wl.KV_FP8, kv_ring=ring,
+                              k_scale=ks, v_scale=vs)])
+    out = st.decode(0, to_dev(q), [to_dev(k)], [None if v is None else to_dev(v)], torch.from_numpy(kv).to("cuda:0"),
+                    int(kv.max()))
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), oracle.decode(q, k, v, kv, W, theta, ring=ring, k_scale=ks, v_scale=vs),
+          "fp8 decode T%d D%d W%d alias%d ring%d" % (T, D, W, alias, ring))
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,W,alias,ring,kv_len,ks,vs", [
+    (3, 1, 8, 2, 512, 0, False, 0, [1, 700, 2048], 0.3, 1.7),
+    (4, 1, 8, 1, 256, 1024, True, 1024, [5000, 1024, 1, 3000], 0.03, 0.03),  # ring
+    (2, 2, 8, 2, 512, 300, False, 301, [303, 9999], 0.25, 2.0),
+])
+def test_fp8_cache_decode_with_append(B, T, Hq, Hkv, D, W, alias, ring, kv_len, ks, vs):
+    """New keys / values are stored as E4M3 codes of x / scale (the oracle's
+    quantiser) and attended to as such; the cache bytes are checked too."""
+    import torch
+    kind = wl.SLIDING if W > 0 else wl.FULL
+    theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
+    kv = np.asarray(kv_len, np.int32)
+    rows = ring if ring else int(kv.max())
+    q = inputs.normal_bf16([770, T, 0], (B, T, Hq, D) if T > 1 else (B, Hq, D))
+    kc = inputs.normal_e4m3([770, T, 1], (B, Hkv, rows, D), ks)
+    vc = None if alias else inputs.normal_e4m3([770, T, 2], (B, Hkv, rows, D), vs)
+    nshape = (B, T, Hkv, D) if T > 1 else (B, Hkv, D)
+    kn = inputs.normal_bf16([770, T, 3], nshape)
+    vn = None if alias else inputs.normal_bf16([770, T, 4], nshape)
+    kw, vw = kc.copy(), None if vc is None else vc.copy()
+    kn4, vn4 = kn.reshape(B, T, Hkv, D), None if vn is None else vn.reshape(B, T, Hkv, D)
+    # two elements of every new key far beyond the E4M3 range at this scale: stored saturated at +-448
+    kn4[..., 0] = inputs.bf16_bits_from_f32(np.array([1000.0], np.float32))[0]
+    kn4[..., 1] = inputs.bf16_bits_from_f32(np.array([-1000.0], np.float32))[0]
+    for b in range(B):
+        for t in range(T):
+            r = (kv[b] - T + t) % ring if ring else kv[b] - T + t
+            kw[b, :, r] = oracle.fp8_e4m3_quantize(inputs.f32_from_bf16_bits(kn4[b, t]), ks)
+            if vw is not None:
+                vw[b, :, r] = oracle.fp8_e4m3_quantize(inputs.f32_from_bf16_bits(vn4[b, t]), vs)
+    st = Stack([wl.layer_desc(kind, D, Hq, Hkv, theta, W, int(alias), kv_dtype=wl.KV_FP8, kv_ring=ring,
+                              k_scale=ks, v_scale=vs)])
+    kd, vd = to_dev(kc), None if vc is None else to_dev(vc)
+    out = st.decode(0, to_dev(q), [kd], [vd], torch.from_numpy(kv).to("cuda:0"), int(kv.max()),
+                    k_new=to_dev(kn), v_new=None if vn is None else to_dev(vn))
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), kw), "E4M3 key cache after the append"
+    if vd is not None:
+        assert np.array_equal(vd.cpu().numpy(), vw), "E4M3 value cache after the append"
+    check(out.cpu().numpy(), oracle.decode(q, kw, vw, kv, W, theta, ring=ring, k_scale=ks, v_scale=vs),
+          "fp8 append T%d D%d ring%d" % (T, D, ring))

@@ -37,6 +37,8 @@ MUTATIONS = {
     "chunk_query_position": ("qpos[nq] = start_pos + s;", "qpos[nq] = s;", None),
     "span_ignored": ("if (j < 0 || j > e || j >= L) return 0;", "if (j < 0 || j > p || j >= L) return 0;", None),
     "verify_all_at_last_position": ("qpos[nq] = L - T + t;", "qpos[nq] = L - 1;", None),
+    "fp8_quantize_ties_to_odd": ("if (dc < db || (dc == db && (c & 1) == 0)) best = c;",
+                                 "if (dc < db || (dc == db && (c & 1) == 1)) best = c;", None),
     "softmax_no_max_shift": ("s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);",
                              "s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m) + 1e-3;", None),
 }

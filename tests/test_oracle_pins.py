@@ -592,3 +592,28 @@ def test_one_span_over_everything_is_unmasked_attention(orc):
     out = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(np.ascontiguousarray(qr)),
                                                            torch.from_numpy(kr), torch.from_numpy(widen(k)))
     assert np.max(np.abs(got - out.numpy().transpose(0, 2, 1, 3))) < 1e-10
+
+
+def test_fp8_quantize_matches_torch_and_saturates(orc):
+    """x / scale in float32 rounded to E4M3 like torch's float8_e4m3fn
+    conversion inside the finite range, saturating to +-448 beyond it."""
+    import torch
+    rng = np.random.default_rng(928)
+    x = np.concatenate([rng.standard_normal(3000).astype(np.float32) * 3,
+                        np.arange(-470, 470, 0.25, dtype=np.float32),
+                        np.array([2 ** -10, 3 * 2 ** -11, 1.5 * 2 ** -9, 2.5 * 2 ** -9, 0.0, -0.0], np.float32)])
+    for scale in (1.0, 0.5, 0.3):
+        got = orc.fp8_e4m3_quantize(x, scale)
+        q = (x / np.float32(scale)).astype(np.float32)
+        inr = np.abs(q) <= 448
+        want = torch.from_numpy(q[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got[inr], want)
+        assert np.all(got[~inr & (q > 0)] == 0x7E) and np.all(got[~inr & (q < 0)] == 0xFE)
+    # every code decodes to the nearest E4M3 value of the quotient
+    vals = orc.fp8_e4m3_value(np.arange(256, dtype=np.uint8))
+    fin = vals[np.isfinite(vals)]
+    q = (x / np.float32(0.3)).astype(np.float32).astype(np.float64)
+    dec = orc.fp8_e4m3_value(orc.fp8_e4m3_quantize(x, 0.3))
+    inr = np.abs(q) <= 448
+    nearest = np.min(np.abs(fin[None, :] - q[inr, None]), axis=1)
+    assert np.allclose(np.abs(dec[inr] - q[inr]), nearest, rtol=0, atol=0)
