@@ -2631,6 +2631,15 @@ static int prefill_split_pv_override() {
   return (v == 0 || v == 1) ? v : -1;
 }
 
+// G4_PREFILL_KPIECES=k pins the number of pieces a work unit's key range is
+// cut into (tests and tuning; unset = cost model).
+static int prefill_kpieces_override() {
+  const char* e = std::getenv("G4_PREFILL_KPIECES");
+  if (!e) return 0;
+  const int v = std::atoi(e);
+  return (v >= 1 && v <= 64) ? v : 0;
+}
+
 PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W, int P0) {
   PrefillPlan p;
   p.BN = prefill_key_tile(D);
@@ -2659,9 +2668,12 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W, int P0) {
         umax = std::max(umax, (a1 - a0 + 1) + (b1 - b0 + 1));
       }
       const long groups = (long)B * Hkv * nunits;
-      const int kmax =
+      int kmax =
           rows == 64 ? 1 : (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
+      if (rows != 64 && prefill_kpieces_override()) kmax = std::min(prefill_kpieces_override(), umax);
+      const int kforced = rows == 64 ? 0 : prefill_kpieces_override();
       for (int k = 1; k <= kmax; ++k) {
+        if (kforced && k != std::min(kforced, umax)) continue;
         const double rounds = std::ceil((double)groups * k / kPrefillSlots);
         const double segs = paired ? (k <= 2 ? 2.0 : 1.5) : 1.0;
         const double t = rounds * (std::ceil((double)umax / k) * c.tile + segs * c.segment + (k > 1 ? c.split : 0.0));
