@@ -408,6 +408,17 @@ struct PrefillArgs {
   RopeRev rope;
 };
 
+// Loads every scalar field of the prefill arguments in one batch at kernel
+// entry.  Left to itself the compiler fetches them where they are first
+// used, behind branches, as a chain of dependent kernel-argument round trips
+// (about 800 cycles of the sliding-layer kernel's start); the empty asm
+// takes all of them as inputs, so they are issued together up front.
+#define G4_PREFETCH_PREFILL_ARGS(a)                                                                                 \
+  asm volatile("" ::"s"((a).q), "s"((a).kimg), "s"((a).vimg), "s"((a).out), "s"((a).counters), "s"((a).part),    \
+               "s"((a).B), "s"((a).S), "s"((a).Hq), "s"((a).Hkv), "s"((a).g), "s"((a).Lmax), "s"((a).W),            \
+               "s"((a).ntiles), "s"((a).nqt), "s"((a).npair), "s"((a).kpieces), "s"((a).P0), "s"((a).paired),      \
+               "s"((a).qscale), "s"((a).vscale), "s"(gridDim.x))
+
 // Causal limit of query sq (at position pos) of batch entry b: the last key
 // it sees -- its own position, or the end of its bidirectional span, clamped
 // to [pos, P0 + S - 1] so that no image row beyond the chunk is ever read.
@@ -446,6 +457,7 @@ __device__ __forceinline__ float max_lane_pair(float x) {  // max over lanes l a
 template <int D, int BN, int DS, bool SPV, bool SPAN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256 * DS, 256 * DS), amdgpu_waves_per_eu(DS, DS))) void
 k_prefill(PrefillArgs a) {
+  G4_PREFETCH_PREFILL_ARGS(a);
   constexpr int NT = 256 * DS;                // threads
   constexpr int NW = 4 * DS;                  // waves
   constexpr int KSTEPS = D / 16;              // 32x32x16 steps over the head dim
@@ -1177,6 +1189,7 @@ __device__ __forceinline__ void mfma16v_last(f32x4& d, const bf16x8& a, const bf
 template <int D, int BN, int ROWS, bool SPAN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 k_prefill4(PrefillArgs a) {
+  G4_PREFETCH_PREFILL_ARGS(a);
   static_assert(ROWS == 128 || ROWS == 64, "query tile of 128 or 64 rows");
   static_assert(D == 256, "one wave per SIMD holds the queries and output block of head size 256 only");
   constexpr bool R64 = ROWS == 64;   // 16 score rows per wave (16x16x32 MFMAs), no split pieces
