@@ -554,15 +554,74 @@ k_prefill(PrefillArgs a) {
     bf16x8 qf[KSW];
     {
       const uint16_t* qrow = a.q + (((size_t)b * a.S + sq) * a.Hq + head) * D;
+      // The g query heads of a position share its rotation.  When the
+      // tile's positions fit, each (position, frequency) pair's cos / sin is
+      // computed once by the work-group into the second key and value
+      // buffers (idle until the first phase barrier of the tile schedule:
+      // the segment's first tile goes to the first buffers) and read back by
+      // every row of that position: the values per-row computation gives,
+      // at 1/g of its double-precision and transcendental work.
+      // Table row pp (position pos_min + pp) holds HF (cos, sin) pairs, two
+      // frequencies per 16-byte slot; the slot index is XOR-swizzled by the
+      // row so that the 16 (position, lane half) combinations one read
+      // instruction touches fall in 16 distinct bank groups.
+      constexpr int HF = D / 2;
+      constexpr int kRowBytes = HF * 8;
+      constexpr int kRowsPerBuf = (int)(sizeof(sk1) / kRowBytes);
+      const int npos = pos_max - pos_min + 1;
+      auto tab_slot = [&](int pp, int col) -> unsigned {  // LDS byte address of (row pp, 16-byte slot col)
+        const int sw = col ^ ((pp & 3) | ((pp & 4) << 1));
+        return (pp < kRowsPerBuf ? lds_addr(sk1) + pp * kRowBytes : lds_addr(sv1) + (pp - kRowsPerBuf) * kRowBytes) +
+               sw * 16;
+      };
+      if (npos <= 2 * kRowsPerBuf) {
+        // this wave's query chunks are loaded first; their latency hides
+        // behind the table fill (rotated in place afterwards)
+        u32x4 xq[KSW / 2], yq[KSW / 2];
 #pragma unroll
-      for (int i = 0; i < KSW / 2; ++i) {
-        const int ks = dp * (KSW / 2) + i;  // first-half step, partner ks + KSTEPS/2
-        const int d0 = 16 * ks + 8 * h;
-        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
-        u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
-        rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
-        qf[i] = as_bf16x8(x);
-        qf[i + KSW / 2] = as_bf16x8(y);
+        for (int i = 0; i < KSW / 2; ++i) {
+          const int d0 = 16 * (dp * (KSW / 2) + i) + 8 * h;
+          xq[i] = *reinterpret_cast<const u32x4*>(qrow + d0);
+          yq[i] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+        }
+        static_assert(NT % HF == 0, "frequencies must tile the work-group");
+        const int f = tid % HF;
+        const double rev = a.rope.rev[f];
+        for (int pp = tid / HF; pp < npos; pp += NT / HF) {
+          float sn, cs;
+          sincos_rev((double)(pos_min + pp), rev, sn, cs);
+          *reinterpret_cast<__attribute__((address_space(3))) f32x2*>(tab_slot(pp, f / 2) + (f & 1) * 8) =
+              f32x2{cs, sn};
+        }
+        lds_barrier();
+        const int pp = pos - pos_min;
+#pragma unroll
+        for (int i = 0; i < KSW / 2; ++i) {
+          const int d0 = 16 * (dp * (KSW / 2) + i) + 8 * h;  // frequencies d0 .. d0 + 7
+          const u32x4 x = xq[i], y = yq[i];
+          u32x4 xo, yo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (cos, sin) of frequencies d0 + 2e and d0 + 2e + 1
+            const f32x4 t = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tab_slot(pp, d0 / 2 + e));
+            const float a0 = bf_lo(x[e]), a1 = bf_hi(x[e]), b0 = bf_lo(y[e]), b1 = bf_hi(y[e]);
+            xo[e] = pack_bf16((a0 * t[0] - b0 * t[1]) * a.qscale, (a1 * t[2] - b1 * t[3]) * a.qscale);
+            yo[e] = pack_bf16((b0 * t[0] + a0 * t[1]) * a.qscale, (b1 * t[2] + a1 * t[3]) * a.qscale);
+          }
+          qf[i] = as_bf16x8(xo);
+          qf[i + KSW / 2] = as_bf16x8(yo);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < KSW / 2; ++i) {
+          const int ks = dp * (KSW / 2) + i;  // first-half step, partner ks + KSTEPS/2
+          const int d0 = 16 * ks + 8 * h;
+          u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+          u32x4 y = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+          rope8(x, y, a.rope.rev, d0, (double)pos, a.qscale);
+          qf[i] = as_bf16x8(x);
+          qf[i + KSW / 2] = as_bf16x8(y);
+        }
       }
     }
 
