@@ -1245,11 +1245,21 @@ __device__ __forceinline__ void mfma16v_last(f32x4& d, const bf16x8& a, const bf
 // iterations i .. i+1, P(i) in exchange buffer i&1 during i .. i+1.
 // The work split over work-groups (pairs of query tiles, pieces of their
 // key work) and the partial-result merge follow k_prefill.
-template <int D, int BN, int ROWS, bool SPAN>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+//
+// PROD (64-row tiles): four more waves, one per SIMD beside each compute
+// wave, issue every tile copy in place of the compute waves.  A
+// direct-to-LDS copy holds its issuing wave until the memory pipeline takes
+// it (about 35 cycles each, eight per wave and tile), time the compute
+// waves otherwise lose inside their score chains.  A producer wave runs a
+// code path of its own with exactly the compute waves' sequence of
+// barriers, and no compute.
+template <int D, int BN, int ROWS, bool SPAN, bool PROD>
+__global__ __attribute__((amdgpu_flat_work_group_size(PROD ? 512 : 256, PROD ? 512 : 256),
+                          amdgpu_waves_per_eu(PROD ? 2 : 1, PROD ? 2 : 1))) void
 k_prefill4(PrefillArgs a) {
   G4_PREFETCH_PREFILL_ARGS(a);
   static_assert(ROWS == 128 || ROWS == 64, "query tile of 128 or 64 rows");
+  static_assert(!PROD || ROWS == 64, "producer waves fit beside the registers of 64-row tiles only");
   static_assert(D == 256, "one wave per SIMD holds the queries and output block of head size 256 only");
   constexpr bool R64 = ROWS == 64;   // 16 score rows per wave (16x16x32 MFMAs), no split pieces
   constexpr int KSTEPS = D / 16;     // 32x32x16 steps over the head dim
@@ -1279,7 +1289,11 @@ k_prefill4(PrefillArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int j16 = lane & 15, grp = lane >> 4;  // 64-row tiles: score lane = (row j16, key group grp)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = PROD && wave_id >= 4;  // wave-uniform
+  // a compute wave, or the compute wave whose share of the copies a producer issues
+  const int wave = PROD ? (wave_id & 3) : wave_id;
+  constexpr int NTH = PROD ? 512 : 256;  // threads
 
   const int nblk = gridDim.x;
   const int wid = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
@@ -1344,11 +1358,69 @@ k_prefill4(PrefillArgs a) {
     // The first two key tiles and the first value tile of a pass, issued
     // together: one memory round trip instead of two.
     auto issue_head = [&]() __attribute__((always_inline)) {
+      if (PROD && !producer) return;
       issue_k(jb, sk[0]);
       issue_v(jb, sv[0]);
       if (1 < nt) issue_k(jb + 1, sk[1]);
     };
     issue_head();  // lands while the queries are loaded and rotated
+
+    // Rotation table of the segment (see below): its positions fit when ...
+    constexpr int HF = D / 2;
+    const int npos = pos_max - pos_min + 1;
+    const bool shared_table = (size_t)npos * HF * sizeof(f32x2) <= sizeof(rtab);
+    auto fill_table = [&]() __attribute__((always_inline)) {
+      // thread t fills frequency t % HF for every (NTH / HF)-th position
+      static_assert(NTH % HF == 0, "frequencies must tile the work-group");
+      const int f = tid % HF;
+      const double rev = a.rope.rev[f];
+#pragma unroll 4
+      for (int pp = tid / HF; pp < npos; pp += NTH / HF) {
+        float sn, cs;
+        sincos_rev((double)(pos_min + pp), rev, sn, cs);
+        rtab[pp * HF + f] = f32x2{cs, sn};
+      }
+    };
+
+    if constexpr (PROD) {
+      if (producer) {
+        // The compute waves' barriers, in order: table fill (when shared),
+        // then per pass: first tile, one per further tile, after the last
+        // tile, two around the vote; then the output's.  Copies go out right
+        // after the barrier that frees their buffers and are waited for
+        // before the next one, as the compute waves did.
+        if (shared_table) {
+          fill_table();
+          lds_barrier();
+        }
+        for (bool first = true;; first = false) {
+          if (!first) issue_head();
+          if (1 < nt)  // key tile jb has landed (copies complete in issue order)
+            wait_vm<2 * LPT>();
+          else
+            wait_vm<LPT>();
+          lds_barrier();
+          for (int i = 1; i < nt; ++i) {
+            wait_vm<0>();
+            lds_barrier();
+#pragma unroll
+            for (int u = 0; u < LPT; ++u) {
+              if (i + 1 < nt) issue_blk(kimg, jb + i + 1, sk[(i + 1) & 1], u);
+              issue_blk(vimg, jb + i, sv[i & 1], u);
+            }
+          }
+          wait_vm<0>();
+          lds_barrier();
+          lds_barrier();  // the compute waves' votes are written
+          const int* vote = reinterpret_cast<const int*>(&sk[1][0]);
+          const bool any = __builtin_amdgcn_readfirstlane(vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+          lds_barrier();
+          if (!any) break;
+        }
+        lds_barrier();  // the row sums of the output
+        return;
+      }
+    }
 
     // Q' = RoPE(q) * scale * log2(e) for this wave's rows, whole head dim:
     // qf[ks] is the B operand of head-dim step ks.  128-row tiles (32x32x16
@@ -1365,9 +1437,6 @@ k_prefill4(PrefillArgs a) {
       // computed once by the work-group into LDS (the idle tile buffers) and
       // read back by every row of that position: the same values as
       // computing them per row, at 1/g of the transcendental work.
-      constexpr int HF = D / 2;
-      const int npos = pos_max - pos_min + 1;
-      const bool shared_table = (size_t)npos * HF * sizeof(f32x2) <= sizeof(rtab);
       if (shared_table) {
         // this wave's query chunks are loaded first; their latency hides
         // behind the table fill (rotated in place afterwards)
@@ -1378,17 +1447,8 @@ k_prefill4(PrefillArgs a) {
           xq[i] = *reinterpret_cast<const u32x4*>(qrow + d0);
           yq[i] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
         }
-        // thread t fills frequency t % HF for every (256 / HF)-th position
         f32x2* tab = rtab;
-        static_assert(256 % HF == 0, "frequencies must tile the work-group");
-        const int f = tid % HF;
-        const double rev = a.rope.rev[f];
-#pragma unroll 4
-        for (int pp = tid / HF; pp < npos; pp += 256 / HF) {
-          float sn, cs;
-          sincos_rev((double)(pos_min + pp), rev, sn, cs);
-          tab[pp * HF + f] = f32x2{cs, sn};
-        }
+        fill_table();
         lds_barrier();
         const f32x4* trow = reinterpret_cast<const f32x4*>(tab + (size_t)(pos - pos_min) * HF);
 #pragma unroll
@@ -1718,7 +1778,7 @@ k_prefill4(PrefillArgs a) {
         // the wave (and with it the MFMA pipe) for hundreds of cycles.
         const bool more = i + 1 < nt;
         scores(sk[i & 1], s, [&] { load_ops(sv[pb], pb, 0, o0); }, [&](int t) {
-          if (t % 2 == 1 && t / 2 < 2 * LPT) {
+          if (!PROD && t % 2 == 1 && t / 2 < 2 * LPT) {
             const int u = t / 2;
             if (u < LPT) {
               if (more) issue_blk(kimg, jb + i + 1, sk[(i + 1) & 1], u);
@@ -2703,6 +2763,15 @@ static int prefill_split_pv_override() {
   return (v == 0 || v == 1) ? v : -1;
 }
 
+// G4_PREFILL_PRODUCER=0 or 1 turns the producer waves of the 64-row
+// head-size-256 kernel off or on (tests reach both; unset = on).
+static int prefill_producer_override() {
+  const char* e = std::getenv("G4_PREFILL_PRODUCER");
+  if (!e) return -1;
+  const int v = std::atoi(e);
+  return (v == 0 || v == 1) ? v : -1;
+}
+
 // G4_PREFILL_KPIECES=k pins the number of pieces a work unit's key range is
 // cut into (tests and tuning; unset = cost model).
 static int prefill_kpieces_override() {
@@ -2843,16 +2912,21 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
       hipLaunchKernelGGL((k_prefill_prep<256, 32, false>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
                          p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
+    const bool prod = prefill_producer_override() != 0;  // 64-row tiles: copies from producer waves
     if (a.span_end != nullptr) {
-      if (pl.rows == 64)
-        hipLaunchKernelGGL((k_prefill4<256, 32, 64, true>), grid_a, dim3(256), 0, stream, a);
+      if (pl.rows == 64 && prod)
+        hipLaunchKernelGGL((k_prefill4<256, 32, 64, true, true>), grid_a, dim3(512), 0, stream, a);
+      else if (pl.rows == 64)
+        hipLaunchKernelGGL((k_prefill4<256, 32, 64, true, false>), grid_a, dim3(256), 0, stream, a);
       else
-        hipLaunchKernelGGL((k_prefill4<256, 32, 128, true>), grid_a, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_prefill4<256, 32, 128, true, false>), grid_a, dim3(256), 0, stream, a);
     } else {
-      if (pl.rows == 64)
-        hipLaunchKernelGGL((k_prefill4<256, 32, 64, false>), grid_a, dim3(256), 0, stream, a);
+      if (pl.rows == 64 && prod)
+        hipLaunchKernelGGL((k_prefill4<256, 32, 64, false, true>), grid_a, dim3(512), 0, stream, a);
+      else if (pl.rows == 64)
+        hipLaunchKernelGGL((k_prefill4<256, 32, 64, false, false>), grid_a, dim3(256), 0, stream, a);
       else
-        hipLaunchKernelGGL((k_prefill4<256, 32, 128, false>), grid_a, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_prefill4<256, 32, 128, false, false>), grid_a, dim3(256), 0, stream, a);
     }
   }
   if (ev.after) (void)hipEventRecord(ev.after, stream);

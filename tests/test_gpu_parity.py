@@ -104,7 +104,7 @@ def test_prefill_head512_schedules(monkeypatch, split_pv, B, S, Hq, Hkv, W, alia
                   Hkv, 512, W, alias, Lmax)
 
 
-@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("rows,producer", [(64, 1), (64, 0), (128, 1)])
 @pytest.mark.parametrize("B,S,Hq,Hkv,W,alias,Lmax", [
     (2, 333, 8, 1, 48, True, 333),      # sliding K=V, batch 2, ragged
     (1, 130, 2, 2, 16, False, 130),     # no GQA sharing, separate V
@@ -116,11 +116,13 @@ def test_prefill_head512_schedules(monkeypatch, split_pv, B, S, Hq, Hkv, W, alia
     (1, 1000, 8, 1, 512, True, 1000),   # the stack's sliding-layer configuration, shorter
     (1, 45, 96, 1, 16, True, 45),       # GQA group of 96: one position per 64-row tile, less than one per row block
 ])
-def test_prefill_head256_tile_heights(monkeypatch, rows, B, S, Hq, Hkv, W, alias, Lmax):
-    """Head size 256 runs 128-row or 64-row query tiles; both against the oracle."""
+def test_prefill_head256_tile_heights(monkeypatch, rows, producer, B, S, Hq, Hkv, W, alias, Lmax):
+    """Head size 256 runs 128-row or 64-row query tiles, the 64-row ones with
+    or without producer waves for the tile copies; all against the oracle."""
     monkeypatch.setenv("G4_PREFILL_ROWS", str(rows))
-    _prefill_case("prefill rows%d B%d S%d Hq%d Hkv%d W%d alias%d" % (rows, B, S, Hq, Hkv, W, alias), B, S, Hq, Hkv,
-                  256, W, alias, Lmax)
+    monkeypatch.setenv("G4_PREFILL_PRODUCER", str(producer))
+    _prefill_case("prefill rows%d producer%d B%d S%d Hq%d Hkv%d W%d alias%d" % (rows, producer, B, S, Hq, Hkv, W, alias),
+                  B, S, Hq, Hkv, 256, W, alias, Lmax)
 
 
 def test_prefill_window_one_is_identity_on_raw_keys():
@@ -393,10 +395,13 @@ def test_wide_range_prefill_head512(monkeypatch, split_pv):
 
 
 @pytest.mark.parametrize("case", [1, 2])
-@pytest.mark.parametrize("rows", [64, 128])
-def test_wide_range_prefill_head256(monkeypatch, rows, case):
+@pytest.mark.parametrize("rows,producer", [(64, 1), (64, 0), (128, 1)])
+def test_wide_range_prefill_head256(monkeypatch, rows, producer, case):
+    """(64-row tiles run with and without their producer waves: the repeated
+    pass must replay the same barrier sequence in both roles.)"""
     monkeypatch.setenv("G4_PREFILL_ROWS", str(rows))
-    _wide_prefill(wri.PREFILL_CASES[case], "wide prefill D256 case%d rows%d" % (case, rows))
+    monkeypatch.setenv("G4_PREFILL_PRODUCER", str(producer))
+    _wide_prefill(wri.PREFILL_CASES[case], "wide prefill D256 case%d rows%d producer%d" % (case, rows, producer))
 
 
 @pytest.mark.parametrize("case", wri.DECODE_CASES)
