@@ -318,7 +318,11 @@ def bench_decode_long(steps, warmup):
 
 def bench_stack(steps):
     """35-layer prefill stack (B=1, S=2048; 28 sliding hd256 W512 K=V + 7 full hd512, 15 owned caches):
-    one pass = every layer's prefill call, in order, on one stream."""
+    one pass = every layer's prefill call, in order, on one stream.  A layer
+    that shares an earlier layer's cache runs in that layer's workspace and
+    reuses the key/value operand images it left there (images_ready): the
+    same cache rotated with the same theta, so its key pass would rebuild
+    them bit for bit."""
     import torch
     from hybrid_sliding_global_amd import Stack, inputs
     from hybrid_sliding_global_amd import workloads as wl
@@ -334,7 +338,10 @@ def bench_stack(steps):
         vs.append(dev(inputs.normal_bf16([4, i, inputs.TENSOR_V], (1, d["num_kv_heads"], S, D)))
                   if own and not d["kv_alias"] else None)
         outs.append(torch.empty((1, S, d["num_q_heads"], D), dtype=torch.float32, device="cuda:0"))
-        wss.append(torch.empty(st.prefill_workspace_bytes(i, 1, S), dtype=torch.uint8, device="cuda:0"))
+        # an owner's workspace also serves the layers sharing its cache
+        need = max(st.prefill_workspace_bytes(j, 1, S) for j, e in enumerate(w.layers)
+                   if j == i or e["kv_source_layer"] == i)
+        wss.append(torch.empty(need, dtype=torch.uint8, device="cuda:0") if own else None)
     flops = sum(wl.prefill_flops(S, d["num_q_heads"], d["head_dim"], d["window"]) for d in w.layers)
     sl_flops = sum(wl.prefill_flops(S, d["num_q_heads"], d["head_dim"], d["window"]) for d in w.layers
                    if d["kind"] == wl.SLIDING)
@@ -342,7 +349,8 @@ def bench_stack(steps):
     def one_pass(which=None):
         for i, d in enumerate(w.layers):
             if which is None or d["kind"] == which:
-                st.prefill(i, qs[i], ks, vs, out=outs[i], workspace=wss[i])
+                src = st.source(i)
+                st.prefill(i, qs[i], ks, vs, out=outs[i], workspace=wss[src], images_ready=src != i)
 
     def timed(fn):
         for _ in range(2):

@@ -61,7 +61,7 @@ class LayerDesc(ctypes.Structure):
 
 
 class PrefillOpts(ctypes.Structure):
-    _fields_ = [("start_pos", ctypes.c_int32), ("span_end", ctypes.c_void_p)]
+    _fields_ = [("start_pos", ctypes.c_int32), ("images_ready", ctypes.c_int32), ("span_end", ctypes.c_void_p)]
 
 
 class DecodeOpts(ctypes.Structure):
@@ -244,7 +244,7 @@ class Stack:
         if start_pos == 0:
             _check(load().gemma4_prefill_workspace_bytes(self.arr, len(self), layer, batch, seq_len, ctypes.byref(n)))
         else:
-            o = PrefillOpts(int(start_pos), None)
+            o = PrefillOpts(start_pos=int(start_pos))
             _check(load().gemma4_prefill_ext_workspace_bytes(self.arr, len(self), layer, batch, seq_len,
                                                              ctypes.byref(o), ctypes.byref(n)))
         return n.value
@@ -261,10 +261,12 @@ class Stack:
         return n.value
 
     def prefill(self, layer: int, q, k_caches, v_caches, out=None, workspace=None, stream=None, start_pos: int = 0,
-                span_end=None):
+                span_end=None, images_ready: bool = False):
         """q: bf16 [B,S,Hq,D] at positions start_pos .. start_pos+S-1; k_caches/v_caches:
         per-layer lists (None for shared / aliased entries); span_end: None, or
-        int32 device [B,S], the last position of each query's bidirectional span."""
+        int32 device [B,S], the last position of each query's bidirectional span;
+        images_ready: ``workspace`` already holds this layer's key/value operand
+        images (an earlier call on the same cache with the same parameters)."""
         import torch
         d = self.layers[layer]
         B, S, Hq, D = q.shape
@@ -277,6 +279,8 @@ class Stack:
         _check_tensor(k, "k_cache", _cache_dtype(d), (B, d["num_kv_heads"], Lmax, d["head_dim"]))
         if not d["kv_alias"]:
             _check_tensor(v_caches[src], "v_cache", _cache_dtype(d), tuple(k.shape))
+        if images_ready and workspace is None:
+            raise ValueError("images_ready needs the workspace that holds the images")
         s = _resolve_stream(stream)
         if out is None:
             out = _alloc_on(s, (B, S, Hq, D), torch.float32, q.device)
@@ -289,11 +293,11 @@ class Stack:
         nbytes = workspace.numel() * workspace.element_size()
         if span_end is not None:
             _check_tensor(span_end, "span_end", torch.int32, (B, S))
-        if start_pos == 0 and span_end is None:
+        if start_pos == 0 and span_end is None and not images_ready:
             _check(load().gemma4_attn_prefill(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax, _ptr(out),
                                               _ptr(workspace), nbytes, int(s.cuda_stream)))
         else:
-            o = PrefillOpts(int(start_pos), _ptr(span_end))
+            o = PrefillOpts(int(start_pos), int(bool(images_ready)), _ptr(span_end))
             _check(load().gemma4_attn_prefill_ext(self.arr, len(self), layer, _ptr(q), kt, vt, B, S, Lmax,
                                                   ctypes.byref(o), _ptr(out), _ptr(workspace), nbytes,
                                                   int(s.cuda_stream)))

@@ -153,7 +153,7 @@ G4_EXPORT int gemma4_kv_bytes(const g4_layer_desc* layers, int32_t n_layers, int
 
 namespace {
 
-const g4_prefill_opts kPrefillDefaults = {0, nullptr};
+const g4_prefill_opts kPrefillDefaults = {0, 0, nullptr};
 const g4_decode_opts kDecodeDefaults = {1, nullptr, nullptr};
 
 int check_prefill_opts(const g4_prefill_opts& o) {
@@ -258,6 +258,7 @@ int prefill_call(const g4_layer_desc* layers, int32_t n_layers, int32_t layer, c
   p.W = d.kind == G4_SLIDING ? d.window : 0;
   p.P0 = o.start_pos;
   p.span_end = o.span_end;
+  p.images_ready = o.images_ready != 0;
   p.fp8 = d.kv_dtype == G4_KV_FP8_E4M3;
   p.k_scale = p.fp8 ? d.k_scale : 1.f;
   p.v_scale = p.fp8 ? (d.kv_alias ? d.k_scale : d.v_scale) : 1.f;

@@ -52,6 +52,7 @@ struct PrefillLaunch {
   int B, S, Hq, Hkv, D, Lmax, W;
   int P0;             // position of query 0: queries P0 .. P0+S-1 over keys 0 .. P0+S-1
   const int32_t* span_end;  // null, or device [B, S]: last position of each query's bidirectional span
+  bool images_ready;  // the workspace already holds this call's key/value operand images: no key pass
   bool fp8;           // the cache holds E4M3 bytes: key element = code * k_scale, value = code * v_scale
   float k_scale, v_scale;  // (v_scale is k_scale for an aliased layer; both 1 for bf16)
   float scale;        // softmax scale (already resolved, > 0)

@@ -390,6 +390,13 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const void* __restrict__ k
   }
 }
 
+// Zeroes the split tiles' arrival counters when the key pass, which
+// otherwise does it, is skipped (images already in the workspace).  A kernel
+// rather than a memset, so that the call can be captured in a HIP graph.
+__global__ __launch_bounds__(256) void k_zero_counters(int* counters, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counters[i] = 0;
+}
+
 // ------------------------------------------------------ prefill: attention --
 
 struct PrefillArgs {
@@ -2886,13 +2893,28 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   const void* vraw = p.v;
   uint16_t* kimg = reinterpret_cast<uint16_t*>(ws);
   uint16_t* vimg = reinterpret_cast<uint16_t*>(ws + pl.vimg_off);
-  if (p.D == 512) {
+  if (p.images_ready) {
+    // the operand images are the workspace's already; only the counters of
+    // split tiles need resetting
+    if (pl.kpieces > 1)
+      hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)std::min<size_t>((pl.ncounters + 255) / 256, 64)), dim3(256), 0,
+                         stream, a.counters, (int)pl.ncounters);
+  } else if (p.D == 512) {
     if (p.fp8)
       hipLaunchKernelGGL((k_prefill_prep<512, 32, true>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
                          p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     else
       hipLaunchKernelGGL((k_prefill_prep<512, 32, false>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
                          p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+  } else {
+    if (p.fp8)
+      hipLaunchKernelGGL((k_prefill_prep<256, 32, true>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
+                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+    else
+      hipLaunchKernelGGL((k_prefill_prep<256, 32, false>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
+                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
+  }
+  if (p.D == 512) {
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     if (a.span_end != nullptr) {
       // (spans run the split-PV schedule at every length: the other one's
@@ -2905,12 +2927,6 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
         hipLaunchKernelGGL((k_prefill<512, 32, 2, false, false>), grid_a, dim3(512), 0, stream, a);
     }
   } else {
-    if (p.fp8)
-      hipLaunchKernelGGL((k_prefill_prep<256, 32, true>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
-                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
-    else
-      hipLaunchKernelGGL((k_prefill_prep<256, 32, false>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
-                         p.P0 + p.S, p.Hkv, p.Lmax, pl.ntiles, a.rope, a.counters, (int)pl.ncounters);
     if (ev.before) (void)hipEventRecord(ev.before, stream);
     const bool prod = prefill_producer_override() != 0;  // 64-row tiles: copies from producer waves
     if (a.span_end != nullptr) {

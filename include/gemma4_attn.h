@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define G4_ABI_VERSION 2
+#define G4_ABI_VERSION 3
 
 /* Status codes (library plumbing; no passage of the pages defines them). */
 #define G4_OK 0
@@ -284,9 +284,22 @@ int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, in
  *              intervals inside the chunk: start_pos + s <= span_end[b][s] <
  *              start_pos + seq_len (values outside are clamped into that
  *              range).  The window test is unchanged.
+ *   images_ready  0, or nonzero when the workspace already holds the key and
+ *              value operand images this call would build, written by an
+ *              earlier prefill call into the same workspace from the same
+ *              cache buffers, with the same head size, kv heads, kv_alias,
+ *              kv_dtype, rope_theta, batch, seq_len and start_pos: the key
+ *              pass is then skipped.  This serves the layers that read a cache
+ *              written by an earlier layer ([FR] Blocker 3, "KV Cache
+ *              Sharing": 20 of the 35 layers share the caches of layers 13
+ *              and 14, and a shared layer of the same kind rotates the same
+ *              raw keys with the same rope_theta), called after that layer
+ *              with its workspace.  The library cannot check the claim:
+ *              images of another cache give wrong results, not an error.
  */
 typedef struct {
   int32_t start_pos;
+  int32_t images_ready;
   const int32_t* span_end;
 } g4_prefill_opts;
 

@@ -68,7 +68,7 @@ def test_every_header_declaration_cites_its_passage():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
     for code, name in [(0, "G4_OK"), (-1, "G4_ERR_INVALID_ARG"), (-2, "G4_ERR_UNSUPPORTED"),
                        (-3, "G4_ERR_BAD_SOURCE"), (-4, "G4_ERR_WORKSPACE"), (-5, "G4_ERR_HIP")]:
         assert L.status_string(code) == name
@@ -255,10 +255,10 @@ def test_compute_calls_reject_bad_arguments_without_gpu(lib):
     assert lib.gemma4_attn_decode(wide, 1, 0, fake, tab, tab, fake, 4, 100, 100, fake, fake, 8, None) \
         == L.G4_ERR_WORKSPACE
     # ext calls: start_pos + seq_len beyond the cache, n_tokens above max_kv_len, reserved options set
-    po = L.PrefillOpts(10, None)
+    po = L.PrefillOpts(start_pos=10)
     assert lib.gemma4_attn_prefill_ext(arr, n, 4, fake, tab, tab, 1, 16, 20, ctypes.byref(po), fake, fake, 1 << 20,
                                        None) == L.G4_ERR_INVALID_ARG
-    po = L.PrefillOpts(-1, None)
+    po = L.PrefillOpts(start_pos=-1)
     assert lib.gemma4_attn_prefill_ext(arr, n, 4, fake, tab, tab, 1, 16, 20, ctypes.byref(po), fake, fake, 1 << 20,
                                        None) == L.G4_ERR_INVALID_ARG
     do = L.DecodeOpts(5, None, None)

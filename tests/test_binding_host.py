@@ -111,3 +111,17 @@ def test_temporaries_follow_the_launch_stream(fake, call, explicit):
     assert lib.streams == [launch.cuda_stream]
     assert len(allocs) == 2  # the output and the workspace
     assert all(t.stream is launch for t in allocs)
+
+
+def test_images_ready_needs_the_workspace_that_holds_them(fake):
+    """Reusing a source layer's operand images only makes sense with the
+    workspace they were written to: the binding refuses to allocate one."""
+    import torch
+    from hybrid_sliding_global_amd import workloads as wl
+    lib, allocs, current = fake
+    st = L.Stack([wl.layer_desc(wl.FULL, 512, 8, 2, 1e6, 0, 0)])
+    k = _FakeTensor((1, 2, 64, 512), torch.bfloat16)
+    q = _FakeTensor((1, 64, 8, 512), torch.bfloat16)
+    with pytest.raises(ValueError):
+        st.prefill(0, q, [k], [k], images_ready=True)
+    assert lib.streams == []

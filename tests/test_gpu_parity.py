@@ -190,6 +190,43 @@ def test_workload4_stack_every_row_and_sharing():
         assert torch.equal(ref, outs[i]), "shared layer %d differs from a copied cache" % i
 
 
+@pytest.mark.parametrize("S,rows", [(640, None), (1000, "128")])
+def test_shared_layers_reuse_source_images(monkeypatch, S, rows):
+    """A layer sharing another's cache (same kind, so the same rotation) may
+    reuse the key/value operand images its source left in the workspace
+    (g4_prefill_opts.images_ready): the key pass is skipped and the output is
+    bit-identical to a call that builds them, and matches the oracle.  S=1000
+    with 128-row tiles cuts tiles into pieces, so the reused workspace's split
+    counters are reset without the key pass."""
+    import torch
+    if rows:
+        monkeypatch.setenv("G4_PREFILL_ROWS", rows)
+    layers, qs, kc, vc = _stack_inputs(S)
+    st = Stack(layers)
+    kd = [None if k is None else to_dev(k) for k in kc]
+    vd = [None if v is None else to_dev(v) for v in vc]
+    # one workspace per layer kind: the last owner of each kind leaves its
+    # images there, and every shared layer of that kind reads the same cache
+    kinds = sorted({d["kind"] for d in layers})
+    ws = {kd_: torch.full((max(st.prefill_workspace_bytes(i, 1, S) for i, d in enumerate(layers) if d["kind"] == kd_),),
+                          0xFF, dtype=torch.uint8, device="cuda:0") for kd_ in kinds}
+    checked = 0
+    for i, d in enumerate(layers):
+        shared = d["kv_source_layer"] >= 0
+        out = st.prefill(i, to_dev(qs[i]), kd, vd, workspace=ws[d["kind"]], images_ready=shared)
+        torch.cuda.synchronize()
+        if not shared:
+            continue
+        ref = st.prefill(i, to_dev(qs[i]), kd, vd)  # fresh workspace: builds the images
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "layer %d: reused images differ" % i
+        if checked < 2 or i in (19, 34):
+            src = d["kv_source_layer"]
+            want = oracle.prefill(qs[i], kc[src], None if d["kv_alias"] else vc[src], d["window"], d["rope_theta"])
+            check(out.cpu().numpy(), want, "reused images layer %d (src %d) S%d" % (i, src, S))
+            checked += 1
+
+
 def test_stack_graph_replays_match_eager():
     """The 35-layer stack (S=640) captured in one HIP graph: every replay, with
     eager calls and synchronisations in between, equals the eager outputs bit
