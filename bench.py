@@ -379,9 +379,14 @@ def bench_stack(steps):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         one_pass()
-    ms = timed(graph.replay)
+    graph_ms = timed(graph.replay)
+    # both ways of issuing a pass are timed; the pass rate is the faster one
+    # (the graph replay has measured slower than eager launches here, by
+    # 1-3 %: its nodes are not issued back to back as a stream's launches are)
+    ms = min(graph_ms, eager_ms)
     res["stack"] = {"ms_per_pass": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12, "algorithmic_flops": flops,
-                    "timing": "one HIP graph replay per pass", "eager_ms_per_pass": eager_ms}
+                    "timing": "one HIP graph replay per pass" if graph_ms <= eager_ms else "eager calls, one stream",
+                    "graph_ms_per_pass": graph_ms, "eager_ms_per_pass": eager_ms}
     return {"workload": "stack35_prefill_s2048", **res}
 
 
@@ -435,9 +440,9 @@ def main():
     if not args.no_stack:
         log("stack: 35-layer prefill S=2048")
         line["stack"] = bench_stack(max(3, args.steps // 4))
-        log("stack: %.3f ms per pass as one graph (%.1f TFLOP/s), %.3f ms eager" %
+        log("stack: %.3f ms per pass (%.1f TFLOP/s): %.3f ms as one graph, %.3f ms eager" %
             (line["stack"]["stack"]["ms_per_pass"], line["stack"]["stack"]["TFLOP/s"],
-             line["stack"]["stack"]["eager_ms_per_pass"]))
+             line["stack"]["stack"]["graph_ms_per_pass"], line["stack"]["stack"]["eager_ms_per_pass"]))
     if not args.no_decode:
         log("decode: B=64 L=8192")
         line["decode"] = bench_decode(max(5, args.steps // 2), 2)
