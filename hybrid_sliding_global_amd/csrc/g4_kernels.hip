@@ -390,13 +390,6 @@ __global__ __launch_bounds__(256) void k_prefill_prep(const void* __restrict__ k
   }
 }
 
-// Zeroes the split tiles' arrival counters when the key pass, which
-// otherwise does it, is skipped (images already in the workspace).  A kernel
-// rather than a memset, so that the call can be captured in a HIP graph.
-__global__ __launch_bounds__(256) void k_zero_counters(int* counters, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counters[i] = 0;
-}
-
 // ------------------------------------------------------ prefill: attention --
 
 struct PrefillArgs {
@@ -1054,9 +1047,16 @@ k_prefill(PrefillArgs a) {
       // The arrival flag lives in the first word of a key buffer: no tile is
       // in flight when it is written and read.
       int* s_last = reinterpret_cast<int*>(sk0);
-      if (tid == 0)
-        *s_last = __hip_atomic_fetch_add(&a.counters[(size_t)bh * a.nqt + qt], 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+      if (tid == 0) {
+        // The last piece also resets the counter (every other piece has
+        // counted in already), so a finished launch leaves all counters zero
+        // for the next call on this workspace, which may skip the key pass
+        // that zeroes them (images_ready).
+        int* ctr = &a.counters[(size_t)bh * a.nqt + qt];
+        const bool is_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+        if (is_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = is_last;
+      }
       __syncthreads();
       const bool last = *s_last != 0;
       __syncthreads();  // the buffer is refilled by the next segment
@@ -1873,9 +1873,12 @@ k_prefill4(PrefillArgs a) {
         }
       const int p0 = pcs[0];
       int* s_last = reinterpret_cast<int*>(&sk[0][0]);
-      if (tid == 0)
-        *s_last = __hip_atomic_fetch_add(&a.counters[(size_t)bh * a.nqt + qt], 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+      if (tid == 0) {  // (the last piece resets the counter, see k_prefill)
+        int* ctr = &a.counters[(size_t)bh * a.nqt + qt];
+        const bool is_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+        if (is_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = is_last;
+      }
       __syncthreads();
       const bool last = __builtin_amdgcn_readfirstlane(*s_last) != 0;
       __syncthreads();
@@ -2894,11 +2897,9 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   uint16_t* kimg = reinterpret_cast<uint16_t*>(ws);
   uint16_t* vimg = reinterpret_cast<uint16_t*>(ws + pl.vimg_off);
   if (p.images_ready) {
-    // the operand images are the workspace's already; only the counters of
-    // split tiles need resetting
-    if (pl.kpieces > 1)
-      hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)std::min<size_t>((pl.ncounters + 255) / 256, 64)), dim3(256), 0,
-                         stream, a.counters, (int)pl.ncounters);
+    // the operand images are the workspace's already, and the split tiles'
+    // counters are zero: the key pass zeroed them, and every merge since
+    // reset the ones it used
   } else if (p.D == 512) {
     if (p.fp8)
       hipLaunchKernelGGL((k_prefill_prep<512, 32, true>), grid_k, dim3(256), 0, stream, kraw, vraw, kimg, vimg,
