@@ -16,7 +16,17 @@ The line also carries:
                 head size 512 plus sliding K=V layer head size 256): KV bytes
                 per second of the split-K kernel against HBM peak;
   stack         the 35-layer prefill stack (2048 tokens): every layer's call
-                in order, with the sliding and full layers also timed apart.
+                in order, with the sliding and full layers also timed apart;
+                shared layers reuse their source layer's operand images;
+  long_decode   decode of 4 sequences with long, unequal contexts;
+  small_prefill the 64-token sliding layer (latency-bound, reported only);
+  hbm_reference torch's own device copy and sum over 2 GiB on this GPU.
+
+Defaults: 100 warm-up steps (the GPU reaches its steady clock only after
+20-30 ms of sustained load) and 100 timed steps.  --no-stack,
+--no-long-decode, --no-small, --no-hbm-reference and --no-cpu-baseline skip
+legs; --calibrate-copy runs only the 1 GiB copy the traffic counters are
+calibrated on.
 """
 import argparse
 import json
@@ -393,8 +403,11 @@ def bench_stack(steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # After idle the GPU takes 20-30 ms of sustained load to reach its steady
+    # clock (headline step 200-220 us at first, 172 us after ~150 steps):
+    # the default warm-up covers that, and 100 timed steps are ~17 ms.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
