@@ -2955,9 +2955,19 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
 // of four partials in flight).
 constexpr int kCombineWideMaxParts = 8;
 
+// G4_DECODE_PIECES=n (1..512) caps the decode split at n work-groups
+// (tuning; unset = 512, two per CU).
+static int decode_pieces_override() {
+  const char* e = std::getenv("G4_DECODE_PIECES");
+  if (!e) return 0;
+  const int v = std::atoi(e);
+  return (v >= 1 && v <= kDecodePieces) ? v : 0;
+}
+
 DecodePlan plan_decode(int /*B*/, int /*Hkv*/, int /*W*/, int /*max_kv_len*/) {
   DecodePlan plan;
-  plan.npieces = kDecodePieces;
+  const int o = decode_pieces_override();
+  plan.npieces = o ? o : kDecodePieces;
   return plan;
 }
 
