@@ -340,6 +340,17 @@ def test_decode_split_invariance():
     assert np.max(np.abs(a[0] - b[0])) < 1e-3
 
 
+@pytest.mark.parametrize("pieces", [1, 3, 37, 512])
+@pytest.mark.parametrize("D,W,alias", [(512, 0, False), (256, 1024, True)])
+def test_decode_piece_counts(monkeypatch, pieces, D, W, alias):
+    """The decode split at the extremes of its piece count (G4_DECODE_PIECES):
+    one work-group for every stream's keys, a few pieces each covering
+    several streams, and the default 512; every count matches the oracle."""
+    monkeypatch.setenv("G4_DECODE_PIECES", str(pieces))
+    _decode_case("decode pieces %d D%d W%d" % (pieces, D, W), B=5, Hq=8, Hkv=2, D=D, W=W, alias=alias,
+                 kv_len=[1, 700, 5000, 33, 2049], Lmax=5000)
+
+
 @pytest.mark.parametrize("split_pv", [0, 1])
 def test_prefill_head512_repeatable(monkeypatch, split_pv):
     """Tiles cut into pieces are merged by whichever piece arrives last, in
