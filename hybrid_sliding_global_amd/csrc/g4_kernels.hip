@@ -2952,8 +2952,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
 
 // Average partials per stream up to which the merge takes a whole head per
 // work-group (its threads then hold 2 (head size 512) or 4 (256) groups
-// of four partials in flight).
-constexpr int kCombineWideMaxParts = 8;
+// of four partials in flight).  Measured on the batched decode's sliding
+// layer (about nine partials per stream): the whole-head merge takes 3 us
+// less than the 64-wide slices.
+constexpr int kCombineWideMaxParts = 12;
 
 // G4_DECODE_PIECES=n (1..512) caps the decode split at n work-groups
 // (tuning; unset = 512, two per CU).
