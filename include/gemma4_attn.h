@@ -46,7 +46,17 @@
  *     launched; gemma4_status_string() names it and gemma4_last_error()
  *     gives the detail for the calling thread;
  *   - calls are thread-safe as long as concurrent calls use distinct
- *     workspaces and outputs.
+ *     workspaces and outputs;
+ *   - tuning and test switches, environment variables read by every call
+ *     and every workspace query (query with the settings the call will
+ *     see): G4_PREFILL_ROWS=64|128 (query-tile height of head size 256),
+ *     G4_PREFILL_SPLIT_PV=0|1 (head-size-512 tile schedule),
+ *     G4_PREFILL_PRODUCER=0|1 (copy-issuing waves of 64-row tiles),
+ *     G4_PREFILL_KPIECES=k (pieces per work unit's key range),
+ *     G4_DECODE_PIECES=n (decode split, n <= 512); unset, or out of range,
+ *     = the library's own choice.  They change how the work is split and
+ *     scheduled, not what is computed: results agree up to fp32 rounding
+ *     order.
  */
 #ifndef GEMMA4_ATTN_H
 #define GEMMA4_ATTN_H
@@ -287,9 +297,10 @@ int gemma4_attn_decode_noalloc(const g4_layer_desc* layers, int32_t n_layers, in
  *   images_ready  0, or nonzero when the workspace already holds the key and
  *              value operand images this call would build, written by an
  *              earlier prefill call into the same workspace from the same
- *              cache buffers, with the same head size, kv heads, kv_alias,
- *              kv_dtype, rope_theta, batch, seq_len and start_pos: the key
- *              pass is then skipped.  This serves the layers that read a cache
+ *              cache buffers, with the same head size, query and kv heads,
+ *              kv_alias, kv_dtype, rope_theta, batch, seq_len and start_pos,
+ *              under the same G4_PREFILL_* settings (the workspace layout
+ *              follows the work split): the key pass is then skipped.  This serves the layers that read a cache
  *              written by an earlier layer ([FR] Blocker 3, "KV Cache
  *              Sharing": 20 of the 35 layers share the caches of layers 13
  *              and 14, and a shared layer of the same kind rotates the same
