@@ -270,6 +270,62 @@ def test_stack_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("S,rows", [(1000, "128"), (1000, None)])
+def test_stack_graph_replays_with_image_reuse(monkeypatch, S, rows):
+    """The launch configuration of the stack benchmark, captured in one HIP
+    graph: every shared layer runs in its source layer's workspace and skips
+    the key pass (images_ready), so nothing zeroes the split tiles' counters
+    inside the graph -- each launch must leave them zero itself.  S=1000 cuts
+    tiles into pieces in the head-size-512 kernel (and, with 128-row tiles,
+    in the head-size-256 one); every replay, with eager passes in between,
+    equals the eager outputs bit for bit."""
+    import torch
+    if rows:
+        monkeypatch.setenv("G4_PREFILL_ROWS", rows)
+    layers, qs, kc, vc = _stack_inputs(S)
+    st = Stack(layers)
+    kd = [None if k is None else to_dev(k) for k in kc]
+    vd = [None if v is None else to_dev(v) for v in vc]
+    qd = [to_dev(q) for q in qs]
+    outs = [torch.empty((1, S, d["num_q_heads"], d["head_dim"]), dtype=torch.float32, device="cuda:0")
+            for d in layers]
+    src = [i if d["kv_source_layer"] < 0 else d["kv_source_layer"] for i, d in enumerate(layers)]
+    need = {}
+    for i in range(len(layers)):
+        need[src[i]] = max(need.get(src[i], 0), st.prefill_workspace_bytes(i, 1, S))
+    wss = {o: torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda:0") for o, n in need.items()}
+
+    def one_pass():
+        for i in range(len(layers)):
+            st.prefill(i, qd[i], kd, vd, out=outs[i], workspace=wss[src[i]], images_ready=src[i] != i)
+
+    one_pass()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for i in (0, 4, 19, 34):  # owners and sharers of both kinds against the oracle
+        d = layers[i]
+        want = oracle.prefill(qs[i], kc[src[i]], None if d["kv_alias"] else vc[src[i]], d["window"], d["rope_theta"])
+        check(eager[i].cpu().numpy(), want, "graph stack layer %d (src %d) S%d rows %s" % (i, src[i], S, rows))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(len(layers)):
+            assert torch.equal(outs[i], eager[i]), "replay %d, layer %d differs from eager" % (rep, i)
+        one_pass()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_alias_equals_explicit_duplicate_values():
     import torch
     S, D = 300, 256
