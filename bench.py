@@ -19,12 +19,16 @@ The line also carries:
                 in order, with the sliding and full layers also timed apart;
                 shared layers reuse their source layer's operand images;
   long_decode   decode of 4 sequences with long, unequal contexts;
+  next_rows     the built NEXT rows against their rooflines: a prefill
+                chunk at a start position, image spans, a 4-token verify
+                step, a ring-cache sliding layer with fused append, E4M3
+                caches;
   small_prefill the 64-token sliding layer (latency-bound, reported only);
   hbm_reference torch's own device copy and sum over 2 GiB on this GPU.
 
 Defaults: 100 warm-up steps (the GPU reaches its steady clock only after
 20-30 ms of sustained load) and 100 timed steps.  --no-stack,
---no-long-decode, --no-small, --no-hbm-reference and --no-cpu-baseline skip
+--no-long-decode, --no-next, --no-small, --no-hbm-reference and --no-cpu-baseline skip
 legs; --calibrate-copy runs only the 1 GiB copy the traffic counters are
 calibrated on.
 """
@@ -326,6 +330,138 @@ def bench_decode_long(steps, warmup):
     }
 
 
+def bench_next(steps, warmup):
+    """The built NEXT rows, each against its roofline: a prefill chunk at a
+    start position, prefill with bidirectional image spans, a 4-token verify
+    step over a frozen cache, a sliding layer on a window-sized ring cache
+    with the new token appended by the call, and E4M3 caches.  Decode caches
+    are flushed from L2/MALL before every call, as in the decode legs."""
+    import torch
+    from hybrid_sliding_global_amd import Stack, inputs
+    from hybrid_sliding_global_amd import workloads as wl
+
+    def dev_u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+    def prefill_entry(workload, flops, call_ms, kern_ms):
+        t = flops / (kern_ms * 1e-3) / 1e12
+        return {"workload": workload, "algorithmic_flops": flops, "ms_per_call": call_ms, "kernel_ms": kern_ms,
+                "TFLOP/s": flops / (call_ms * 1e-3) / 1e12,
+                "roofline": {"bound": "mfma", "achieved": t, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": t / PEAK_BF16_TFLOPS}}
+
+    def decode_entry(workload, nbytes, call_ms, kern_ms):
+        g = nbytes / (kern_ms * 1e-3) / 1e9
+        return {"workload": workload, "bytes": nbytes, "ms_per_call": call_ms, "kernel_ms": kern_ms,
+                "GB/s": nbytes / (call_ms * 1e-3) / 1e9,
+                "roofline": {"bound": "hbm", "achieved": g, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": g / PEAK_HBM_GBS}}
+
+    res = {}
+    D, Hq, Hkv = 512, 8, 2
+    full = wl.layer_desc(wl.FULL, D, Hq, Hkv, wl.THETA_FULL, 0, 0)
+    st = Stack([full])
+
+    # chunked prefill: 2048 queries at positions 2048..4095 against a 4096-key cache
+    P0, S = 2048, 2048
+    q = dev(inputs.normal_bf16([6, 0, inputs.TENSOR_Q], (1, S, Hq, D)))
+    k = dev(inputs.normal_bf16([6, 0, inputs.TENSOR_K], (1, Hkv, P0 + S, D)))
+    v = dev(inputs.normal_bf16([6, 0, inputs.TENSOR_V], (1, Hkv, P0 + S, D)))
+    out = torch.empty((1, S, Hq, D), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(st.prefill_workspace_bytes(0, 1, S, P0), dtype=torch.uint8, device="cuda:0")
+    call_ms, kern_ms = time_calls(lambda: st.prefill(0, q, [k], [v], out=out, workspace=ws, start_pos=P0),
+                                  steps, warmup)
+    res["chunked_prefill"] = prefill_entry(
+        "full layer hd512 Hq8/Hkv2, a 2048-token chunk at position 2048 (4096 cached keys)",
+        4 * D * Hq * (S * P0 + S * (S + 1) // 2), call_ms, kern_ms)
+    del q, k, v, out, ws
+
+    # bidirectional spans: the 4096-token full layer with two image spans
+    S = 4096
+    spans = [(512, 1535), (2048, 2559)]
+    span_end = np.arange(S, dtype=np.int32)
+    for a0, a1 in spans:
+        span_end[a0:a1 + 1] = a1
+    q = dev(inputs.normal_bf16([6, 1, inputs.TENSOR_Q], (1, S, Hq, D)))
+    k = dev(inputs.normal_bf16([6, 1, inputs.TENSOR_K], (1, Hkv, S, D)))
+    v = dev(inputs.normal_bf16([6, 1, inputs.TENSOR_V], (1, Hkv, S, D)))
+    se = torch.from_numpy(span_end.reshape(1, S)).to("cuda:0")
+    out = torch.empty((1, S, Hq, D), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(st.prefill_workspace_bytes(0, 1, S), dtype=torch.uint8, device="cuda:0")
+    call_ms, kern_ms = time_calls(lambda: st.prefill(0, q, [k], [v], out=out, workspace=ws, span_end=se),
+                                  steps, warmup)
+    visible = np.minimum(np.maximum(span_end.astype(np.int64), np.arange(S)), S - 1) + 1
+    res["bidirectional_spans"] = prefill_entry(
+        "full layer hd512 Hq8/Hkv2, 4096 tokens, image spans %s (bidirectional inside a span)" % spans,
+        4 * D * Hq * int(visible.sum()), call_ms, kern_ms)
+    del q, k, v, se, out, ws
+
+    flush = make_flush()
+    B, L, T = 64, 8192, 4
+    kv = np.full(B, L, np.int32)
+    kl = torch.from_numpy(kv).to("cuda:0")
+
+    # verify: 4 query tokens per sequence over a frozen 8192-token cache
+    q = dev(inputs.normal_bf16([7, 0, inputs.TENSOR_Q], (B, T, Hq, D)))
+    k = dev(inputs.normal_bf16([7, 0, inputs.TENSOR_K], (B, Hkv, L, D)))
+    v = dev(inputs.normal_bf16([7, 0, inputs.TENSOR_V], (B, Hkv, L, D)))
+    out = torch.empty((B, T, Hq, D), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(st.decode_workspace_bytes(0, B, L, T), dtype=torch.uint8, device="cuda:0")
+    call_ms, kern_ms = time_calls(lambda: st.decode(0, q, [k], [v], kl, L, out=out, workspace=ws),
+                                  steps, 2, flush=flush)
+    nbytes = B * Hkv * L * D * 2 * 2 + T * B * Hq * D * (2 + 4) + B * 4
+    res["verify_decode"] = decode_entry(
+        "B=64 full layer hd512 Hq8/Hkv2, 4 query tokens per sequence over a frozen 8192-token cache",
+        nbytes, call_ms, kern_ms)
+    del q, k, v, out, ws
+
+    # ring: the batched decode's sliding layer on a 1024-row ring, new token appended by the call
+    Ds, Hqs, W = 256, 8, 1024
+    ring = wl.layer_desc(wl.SLIDING, Ds, Hqs, 1, wl.THETA_SLIDING, W, 1, kv_ring=W)
+    st_r = Stack([ring])
+    q = dev(inputs.normal_bf16([7, 1, inputs.TENSOR_Q], (B, Hqs, Ds)))
+    k = dev(inputs.normal_bf16([7, 1, inputs.TENSOR_K], (B, 1, W, Ds)))
+    kn = dev(inputs.normal_bf16([7, 1, inputs.TENSOR_V], (B, 1, Ds)))
+    out = torch.empty((B, Hqs, Ds), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(st_r.decode_workspace_bytes(0, B, L), dtype=torch.uint8, device="cuda:0")
+    call_ms, kern_ms = time_calls(lambda: st_r.decode(0, q, [k], [None], kl, L, out=out, workspace=ws, k_new=kn),
+                                  steps, 2, flush=flush)
+    nbytes = B * (W - 1) * Ds * 2 + B * Ds * 2 * 2 + B * Hqs * Ds * (2 + 4) + B * 4  # ring rows + new key in/out
+    res["ring_append_decode"] = decode_entry(
+        "B=64 sliding layer hd256 Hq8/Hkv1 W=1024 K=V on a 1024-row ring at position 8191, "
+        "the new token's key written by the call", nbytes, call_ms, kern_ms)
+    del q, k, kn, out, ws
+
+    # E4M3 caches: the batched decode workload with one byte per cache element
+    layers = {}
+    total_bytes, total_ms = 0, 0.0
+    for name, (Dl, Hql, Hkvl, Wl, alias, ks, vs) in (("full", (512, 8, 2, 0, 0, 0.125, 0.25)),
+                                                      ("sliding", (256, 8, 1, 1024, 1, 0.125, 0.125))):
+        kind = wl.FULL if Wl == 0 else wl.SLIDING
+        theta = wl.THETA_FULL if Wl == 0 else wl.THETA_SLIDING
+        d8 = wl.layer_desc(kind, Dl, Hql, Hkvl, theta, Wl, alias, kv_dtype=wl.KV_FP8, k_scale=ks, v_scale=vs)
+        st8 = Stack([d8])
+        q = dev(inputs.normal_bf16([8, Dl, inputs.TENSOR_Q], (B, Hql, Dl)))
+        k = dev_u8(inputs.normal_e4m3([8, Dl, inputs.TENSOR_K], (B, Hkvl, L, Dl), ks))
+        v = None if alias else dev_u8(inputs.normal_e4m3([8, Dl, inputs.TENSOR_V], (B, Hkvl, L, Dl), vs))
+        out = torch.empty((B, Hql, Dl), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(st8.decode_workspace_bytes(0, B, L), dtype=torch.uint8, device="cuda:0")
+        call_ms, kern_ms = time_calls(lambda: st8.decode(0, q, [k], [v], kl, L, out=out, workspace=ws),
+                                      steps, 2, flush=flush)
+        keys = min(L, Wl) if Wl > 0 else L
+        nbytes = B * Hkvl * keys * Dl * (1 if alias else 2) + B * Hql * Dl * (2 + 4) + B * 4
+        layers[name] = decode_entry("", nbytes, call_ms, kern_ms)
+        del layers[name]["workload"]
+        total_bytes += nbytes
+        total_ms += call_ms
+        del q, k, v, out, ws
+    res["fp8_decode"] = {
+        "workload": "decode_b64_l8192 with E4M3 caches (one byte per element, per-tensor scales)",
+        "GB/s": total_bytes / (total_ms * 1e-3) / 1e9, "layers": layers,
+        "roofline": layers["full"]["roofline"]}
+    return res
+
+
 def bench_stack(steps):
     """35-layer prefill stack (B=1, S=2048; 28 sliding hd256 W512 K=V + 7 full hd512, 15 owned caches):
     one pass = every layer's prefill call, in order, on one stream.  A layer
@@ -414,6 +550,7 @@ def main():
     ap.add_argument("--no-long-decode", action="store_true")
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-hbm-reference", action="store_true")
+    ap.add_argument("--no-next", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -467,6 +604,10 @@ def main():
         log("decode long: full-layer kernel %.1f GB/s, sliding-layer kernel %.1f GB/s" %
             (line["long_decode"]["layers"]["full"]["kernel_GB/s"],
              line["long_decode"]["layers"]["sliding"]["kernel_GB/s"]))
+    if not args.no_next:
+        log("next rows: chunked prefill, spans, verify, ring append, E4M3 caches")
+        line["next_rows"] = bench_next(max(5, args.steps // 4), 5)
+        log("next rows: %s" % json.dumps({k: round(v["roofline"]["frac"], 3) for k, v in line["next_rows"].items()}))
     if not args.no_small:
         log("small prefill: S=64 sliding layer")
         line["small_prefill"] = bench_small_prefill(max(10, args.steps), args.warmup)

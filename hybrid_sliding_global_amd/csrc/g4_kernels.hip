@@ -84,13 +84,14 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 // Eight E4M3 bytes (OCP encoding, what gfx950's conversions read) -> eight
 // packed bf16: exact, since every E4M3 value is a bf16 value.
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+  // one instruction per pair (scale 1: every E4M3 value, subnormals included,
+  // is exactly a bf16 value; checked bit for bit against the E4M3 -> fp32 ->
+  // bf16 route on all 256 codes)
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-    r[2 * i] = pack_bf16(lo[0], lo[1]);
-    r[2 * i + 1] = pack_bf16(hi[0], hi[1]);
+    r[2 * i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    r[2 * i + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
   }
   return r;
 }
@@ -2136,6 +2137,26 @@ __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
                                                    0, 0);
 }
 
+// The same rotation for 8 (x, y) pairs held as E4M3 bytes: each byte pair
+// goes straight to fp32 (exact) and the rotated pair to packed bf16, the
+// values rot8_const gives on the bf16 form of the same bytes.
+__device__ __forceinline__ void rot8_const_e4m3(u32x2 x8, u32x2 y8, const float* cs, u32x4& xo, u32x4& yo) {
+  f32x2 a[4], b[4];  // element pairs 2e, 2e + 1: bytes of word e / 2, its low or high half
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    a[2 * w] = __builtin_amdgcn_cvt_pk_f32_fp8((int)x8[w], false);
+    a[2 * w + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)x8[w], true);
+    b[2 * w] = __builtin_amdgcn_cvt_pk_f32_fp8((int)y8[w], false);
+    b[2 * w + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)y8[w], true);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float c0 = cs[4 * e], s0 = cs[4 * e + 1], c1 = cs[4 * e + 2], s1 = cs[4 * e + 3];
+    xo[e] = pack_bf16(a[e][0] * c0 - b[e][0] * s0, a[e][1] * c1 - b[e][1] * s1);
+    yo[e] = pack_bf16(b[e][0] * c0 + a[e][0] * s0, b[e][1] * c1 + a[e][1] * s1);
+  }
+}
+
 // max over the four 16-lane groups that share a query column
 __device__ __forceinline__ float max_over_groups(float x) {
   auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -2458,13 +2479,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
                                 kra + ((((d + D / 2) >> 4) ^ ksw) << 4) + ((d + D / 2) & 8)};
         u32x2 f8[2];
         lds_read_b64x2(f8, ad);
-        fr[0] = fp8x8_to_bf16(f8[0]);
-        fr[1] = fp8x8_to_bf16(f8[1]);
+        rot8_const_e4m3(f8[0], f8[1], kcs[kk], fr[0], fr[1]);
       } else {
         const unsigned ad[2] = {kra + (((d >> 3) ^ ksw) << 4), kra + ((((d + D / 2) >> 3) ^ ksw) << 4)};
         lds_read_b128x2(fr, ad);
+        rot8_const(fr[0], fr[1], kcs[kk]);
       }
-      rot8_const(fr[0], fr[1], kcs[kk]);
       sp = mfma16(as_bf16x8(fr[0]), qf[kk], sp);
       sp = mfma16(as_bf16x8(fr[1]), qf[kk + KH], sp);
     }
