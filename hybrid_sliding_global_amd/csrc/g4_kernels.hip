@@ -2260,13 +2260,17 @@ __device__ void decode_split(const DecodeArgs& a, long long& T, int& np, int& b_
 // Key/value rows stream through NSTAGE LDS stages of 16 rows each.
 // GEN = false is the one-token path over a cache of one row per position
 // with nothing appended (T = 1, ring = 0, knew = null): the per-column
-// positions, masks, ring rows and appended rows compile away.  FP8: the
+// positions, masks, ring rows and appended rows compile away.  RA = false
+// (with GEN) is T > 1 tokens over such a cache: only the ring rows and
+// appended rows compile away, whose per-load row arithmetic costs a
+// verify step over a frozen cache about 5 % of its time.  FP8: the
 // cache holds E4M3 bytes; a lane converts its key elements in registers
 // before rotating them, and each stage's values are converted once into a
 // bf16 tile laid out like a bf16 stage, which the value reads then use (the
 // key scale is in qscale, the value scale in the output).
-template <int D, bool ALIAS, int NSTAGE, bool GEN, bool FP8>
+template <int D, bool ALIAS, int NSTAGE, bool GEN, bool FP8, bool RA>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(DecodeArgs a) {
+  static_assert(GEN || !RA, "ring rows and appended rows belong to the general path");
   constexpr int KPS = 16;            // keys per step
   constexpr int FQ = D / 8;          // rotation pairs per wave
   constexpr int KH = FQ / 32;        // groups of 8 pairs per lane (x and y halves each)
@@ -2315,11 +2319,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
   const size_t slice = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   // Keys of the T current tokens come from the appended rows when the call
   // writes them (k_decode_combine stores them into the cache afterwards).
-  const int new0 = GEN && !FP8 && a.knew != nullptr ? L - a.T : 0x7fffffff;
+  const int new0 = RA && !FP8 && a.knew != nullptr ? L - a.T : 0x7fffffff;
   // Cache row of key position pos of this segment: row0 + (pos - k_start),
   // wrapped once for a ring (a segment spans at most the ring's length).
-  const int wrap = GEN && a.ring > 0 ? a.ring : 0x7fffffff;
-  const int row0 = GEN && a.ring > 0 ? k_start % a.ring : k_start;
+  const int wrap = RA && a.ring > 0 ? a.ring : 0x7fffffff;
+  const int row0 = RA && a.ring > 0 ? k_start % a.ring : k_start;
   auto issue = [&](int step, int stg) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -2336,7 +2340,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void k_decode(
         const int row = byte / ROWB, slot = (byte % ROWB) >> 4;
         const int pos = min(k0 + row, k_end - 1);  // key position
         const char* src;
-        if constexpr (GEN) {
+        if constexpr (RA) {
           int crow = row0 + (pos - k_start);
           crow = crow >= wrap ? crow - wrap : crow;
           // (appended rows are bf16 and read here only for a bf16 cache; an
@@ -3048,6 +3052,7 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
   }
   if (ev.before) (void)hipEventRecord(ev.before, stream);
   const bool gen = p.T > 1 || p.ring > 0 || a.knew != nullptr;
+  const bool ring_or_append = p.ring > 0 || a.knew != nullptr;
   auto run = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
   // LDS stages: 4 of 16 rows, except head size 512 with separate K and V
   // (2 of bf16, 3 of E4M3 beside the converted value tile), so that two
@@ -3056,7 +3061,12 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream, const Profil
     constexpr int D = decltype(d_c)::value;
     constexpr bool AL = decltype(alias_c)::value, F8 = decltype(fp8_c)::value;
     constexpr int NS = (D == 512 && !AL) ? (F8 ? 3 : 2) : kDecodeStages;
-    gen ? run(k_decode<D, AL, NS, true, F8>) : run(k_decode<D, AL, NS, false, F8>);
+    if (!gen)
+      run(k_decode<D, AL, NS, false, F8, false>);
+    else if (ring_or_append)
+      run(k_decode<D, AL, NS, true, F8, true>);
+    else
+      run(k_decode<D, AL, NS, true, F8, false>);
   };
   using D512 = std::integral_constant<int, 512>;
   using D256 = std::integral_constant<int, 256>;
