@@ -708,14 +708,16 @@ def _span_end(B, S, P0, spans_per_batch):
     (1, 300, 0, 8, 2, 512, 0, False, [[(10, 290)]], ("G4_PREFILL_SPLIT_PV", "0")),  # short segments, spans
     (2, 700, 0, 8, 1, 256, 0, True, [[(64, 319)], [(5, 6), (200, 455)]], ("G4_PREFILL_ROWS", "64")),
     (2, 700, 0, 8, 1, 256, 0, True, [[(64, 319)], [(5, 6), (200, 455)]], ("G4_PREFILL_ROWS", "128")),
+    (2, 700, 0, 8, 1, 256, 0, True, [[(64, 319)], [(5, 6), (200, 455)]],
+     [("G4_PREFILL_ROWS", "64"), ("G4_PREFILL_PRODUCER", "0")]),  # 64-row tiles, copies from the compute waves
     (1, 500, 0, 8, 1, 256, 64, True, [[(100, 300)]], None),          # a span longer than the window
     (1, 256, 900, 8, 2, 512, 0, False, [[(950, 1100)]], None),        # a chunk at a start position
     (1, 1024, 0, 8, 1, 256, 0, False, [[(300, 900)]], ("G4_PREFILL_ROWS", "128")),  # tiles cut into pieces
 ])
 def test_bidirectional_spans(monkeypatch, B, S, P0, Hq, Hkv, D, W, alias, spans, override):
     import torch
-    if override:
-        monkeypatch.setenv(*override)
+    for name, value in ([override] if override and isinstance(override[0], str) else override or []):
+        monkeypatch.setenv(name, value)
     Lmax = P0 + S
     kind = wl.SLIDING if W > 0 else wl.FULL
     theta = wl.THETA_SLIDING if kind == wl.SLIDING else wl.THETA_FULL
