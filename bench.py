@@ -26,8 +26,10 @@ The line also carries:
   small_prefill the 64-token sliding layer (latency-bound, reported only);
   hbm_reference torch's own device copy and sum over 2 GiB on this GPU.
 
-Defaults: 100 warm-up steps (the GPU reaches its steady clock only after
-20-30 ms of sustained load) and 100 timed steps.  --no-stack,
+Defaults: 100 warm-up and 100 timed steps.  Before its warm-up each leg runs
+its own call, untimed, for SETTLE_MS of wall time: the GPU reaches its steady
+clock only after 20-30 ms of sustained load, so short runs (--warmup 5) would
+otherwise time the clock ramp.  --no-stack,
 --no-long-decode, --no-next, --no-small, --no-hbm-reference and --no-cpu-baseline skip
 legs; --calibrate-copy runs only the 1 GiB copy the traffic counters are
 calibrated on.
@@ -74,6 +76,27 @@ def measured_traffic(kernel):
         return None
 
 
+# After idle the GPU needs 20-30 ms of sustained load to reach its steady
+# clock (the headline step runs at 200-220 us over its first ~50 steps and at
+# ~172 us from ~150 steps on).  Every timed leg first runs its own call,
+# untimed, for this much wall time, and then its warm-up steps.
+SETTLE_MS = 60.0
+
+
+def settle_clock(fn, min_ms=SETTLE_MS):
+    """Untimed calls of fn, in batches of 8, until min_ms of wall time has passed; returns the call count."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return n
+
+
 def time_calls(fn, steps, warmup, flush=None):
     """Average time per call (events around each call) and per main kernel
     (events the library records immediately around it).  The two are taken on
@@ -81,6 +104,7 @@ def time_calls(fn, steps, warmup, flush=None):
     own."""
     import torch
     from hybrid_sliding_global_amd import _lib
+    settle_clock(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -131,6 +155,7 @@ def bench_prefill(steps, warmup):
         st.prefill(0, q, [k], [v], out=out, workspace=ws)
 
     # timed region: K steps bracketed by synchronize
+    settle = settle_clock(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -144,7 +169,8 @@ def bench_prefill(steps, warmup):
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / steps
     _, kern_ms = time_calls(step, steps, 2)
-    return dict(flops=flops, ms_per_step=ms_per_step, wall=wall, kern_ms=kern_ms, q=q_h, k=k_h, v=v_h, w=w)
+    return dict(flops=flops, ms_per_step=ms_per_step, wall=wall, kern_ms=kern_ms, q=q_h, k=k_h, v=v_h, w=w,
+                settle_steps=settle)
 
 
 def cpu_baseline(pre, budget_s=15.0):
@@ -499,6 +525,7 @@ def bench_stack(steps):
                 st.prefill(i, qs[i], ks, vs, out=outs[i], workspace=wss[src], images_ready=src != i)
 
     def timed(fn):
+        settle_clock(fn)
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
@@ -539,9 +566,7 @@ def bench_stack(steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # After idle the GPU takes 20-30 ms of sustained load to reach its steady
-    # clock (headline step 200-220 us at first, 172 us after ~150 steps):
-    # the default warm-up covers that, and 100 timed steps are ~17 ms.
+    # each leg settles the clock first (SETTLE_MS); 100 timed steps are ~17 ms
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -580,6 +605,8 @@ def main():
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "clock_settle": {"min_ms": SETTLE_MS, "headline_steps": pre["settle_steps"],
+                         "note": "untimed calls before each leg's warm-up, until the GPU clock has left its idle ramp"},
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)",
         "config": {"workload": "full_prefill_s4096", "batch": 1, "seq_len": 4096, "q_heads": 8, "kv_heads": 2,
                    "head_dim": 512, "window": 0, "rope_theta": 1e6, "kv_alias": False,
