@@ -622,18 +622,18 @@ def main():
              line["stack"]["stack"]["graph_ms_per_pass"], line["stack"]["stack"]["eager_ms_per_pass"]))
     if not args.no_decode:
         log("decode: B=64 L=8192")
-        line["decode"] = bench_decode(max(5, args.steps // 2), 2)
+        line["decode"] = bench_decode(max(50, args.steps // 2), 2)  # short calls: enough samples for a stable mean
         log("decode: %.1f GB/s (full-layer kernel %.1f GB/s)" %
             (line["decode"]["value"], line["decode"]["layers"]["full"]["kernel_GB/s"]))
     if not args.no_decode and not args.no_long_decode:
         log("decode: B=4, long contexts")
-        line["long_decode"] = bench_decode_long(max(5, args.steps // 2), 2)
+        line["long_decode"] = bench_decode_long(max(50, args.steps // 2), 2)
         log("decode long: full-layer kernel %.1f GB/s, sliding-layer kernel %.1f GB/s" %
             (line["long_decode"]["layers"]["full"]["kernel_GB/s"],
              line["long_decode"]["layers"]["sliding"]["kernel_GB/s"]))
     if not args.no_next:
         log("next rows: chunked prefill, spans, verify, ring append, E4M3 caches")
-        line["next_rows"] = bench_next(max(5, args.steps // 4), 5)
+        line["next_rows"] = bench_next(max(20, args.steps // 4), 5)
         log("next rows: %s" % json.dumps({k: round(v["roofline"]["frac"], 3) for k, v in line["next_rows"].items()}))
     if not args.no_small:
         log("small prefill: S=64 sliding layer")
