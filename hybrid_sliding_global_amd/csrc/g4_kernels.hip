@@ -67,6 +67,19 @@ constexpr int kDecodeStages = 4;      // 16-row key/value stages in the decode L
 
 // ---------------------------------------------------------------- helpers --
 
+// Division by a divisor d >= 1 fixed for a launch (set up on the host), for
+// dividends n in [0, 2^31): q = (n * m) >> s with s = 31 + ceil(log2 d) and
+// m = ceil(2^s / d), which is below 2^32.  Exact: n * m / 2^s exceeds n / d
+// by less than n / 2^s < 2^-ceil(log2 d) <= 1 / d, too little to reach the
+// next integer.  Three scalar instructions instead of the ~25 of a division
+// by a run-time value (the work-group prologues hold a dozen of them).
+struct FastDiv {
+  unsigned m, s;
+};
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  return (int)(((unsigned long long)(unsigned)n * f.m) >> f.s);
+}
+
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -275,7 +288,14 @@ __device__ __forceinline__ void lds_mfma_pipeline() {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+  // (both operands are wave-uniform; readfirstlane says so where the
+  // compiler cannot prove it, and folds away where it can)
+  const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
+  const unsigned long long gu =
+      ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(g >> 32)) << 32) |
+      (unsigned)__builtin_amdgcn_readfirstlane((unsigned)g);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(reinterpret_cast<const void*>(gu)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -404,6 +424,7 @@ struct PrefillArgs {
   int P0;      // position of query 0 (keys 0 .. P0 + S - 1 are visible to the chunk)
   const int32_t* span_end;  // null (causal), or [B, S]: the last position of each query's bidirectional span
   int paired;  // 1: work unit = query tiles t and nqt-1-t; 0: one query tile
+  FastDiv fd_g, fd_kp, fd_pbh, fd_hkv;  // division by g, kpieces, npair * kpieces, Hkv
   float qscale;  // softmax scale * log2(e) (times the key scale of an E4M3 cache): scores in log2 units
   float vscale;  // the value scale of an E4M3 cache (1 otherwise): multiplies every output
   RopeRev rope;
@@ -490,14 +511,15 @@ k_prefill(PrefillArgs a) {
   const int nblk = gridDim.x;
   const int wid = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int per_bh = a.npair * a.kpieces;
-  const int bh = wid / per_bh, rem = wid % per_bh, pair = rem / a.kpieces, piece = rem % a.kpieces;
-  const int kvh = bh % a.Hkv, b = bh / a.Hkv;
+  const int bh = fdiv(wid, a.fd_pbh), rem = wid - bh * per_bh;
+  const int pair = fdiv(rem, a.fd_kp), piece = rem - pair * a.kpieces;
+  const int b = fdiv(bh, a.fd_hkv), kvh = bh - b * a.Hkv;
   const int rows_total = a.S * a.g;
   const bool windowed = a.W > 0;
 
   auto tile_keys = [&](int qt, int& jlo, int& jhi) {
     const int r0 = qt * 128;
-    const int pmin = a.P0 + r0 / a.g, pmax = a.P0 + min(r0 + 127, rows_total - 1) / a.g;
+    const int pmin = a.P0 + fdiv(r0, a.fd_g), pmax = a.P0 + fdiv(min(r0 + 127, rows_total - 1), a.fd_g);
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = causal_limit<SPAN>(a, b, pmax - a.P0, pmax) / BN;
   };
@@ -507,7 +529,7 @@ k_prefill(PrefillArgs a) {
   tile_keys(tl, jlo_l, jhi_l);
   if (ts >= 0) tile_keys(ts, jlo_s, jhi_s);
   const int nL = jhi_l - jlo_l + 1, nS = ts >= 0 ? jhi_s - jlo_s + 1 : 0, U = nL + nS;
-  auto ubound = [&](int j) { return (int)(((long long)j * U) / a.kpieces); };
+  auto ubound = [&](int j) { return fdiv(j * U, a.fd_kp); };  // j * U < 2^31 (the planner caps kpieces)
   const int u0 = ubound(piece), u1 = ubound(piece + 1);
 
   const size_t slice_off = (size_t)(b * a.Hkv + kvh) * a.ntiles * (size_t)(BN * D);
@@ -541,10 +563,10 @@ k_prefill(PrefillArgs a) {
     const int r = r0 + rg * 32 + n;
     const bool valid = r < rows_total;
     const int rc = valid ? r : rows_total - 1;
-    const int sq = rc / a.g, head = kvh * a.g + rc % a.g;  // query index within the chunk
+    const int sq = fdiv(rc, a.fd_g), head = kvh * a.g + (rc - sq * a.g);  // query index within the chunk
     const int pos = a.P0 + sq;                               // its position in the sequence
-    const int pos_min = a.P0 + r0 / a.g;
-    const int pos_max = a.P0 + min(r0 + 127, rows_total - 1) / a.g;
+    const int pos_min = a.P0 + fdiv(r0, a.fd_g);
+    const int pos_max = a.P0 + fdiv(min(r0 + 127, rows_total - 1), a.fd_g);
     const int lim = causal_limit<SPAN>(a, b, sq, pos);                      // this row's last visible key
     const int lim_min = causal_limit<SPAN>(a, b, pos_min - a.P0, pos_min);  // the smallest limit of the tile
 
@@ -1182,7 +1204,7 @@ k_prefill(PrefillArgs a) {
     // through the tile loop, where every register is taken)
     const int r_o = __builtin_amdgcn_readfirstlane(r0) + rg * 32 + n;
     if (r_o < rows_total) {
-      const int sq_o = r_o / a.g, head_o = kvh * a.g + r_o % a.g;
+      const int sq_o = fdiv(r_o, a.fd_g), head_o = kvh * a.g + (r_o - sq_o * a.g);
       float* orow = a.out + (((size_t)b * a.S + sq_o) * a.Hq + head_o) * D + 32 * dp * DBW;
 #pragma unroll
       for (int db = 0; db < DBW; ++db)
@@ -1306,14 +1328,18 @@ k_prefill4(PrefillArgs a) {
   const int nblk = gridDim.x;
   const int wid = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int per_bh = a.npair * a.kpieces;
-  const int bh = wid / per_bh, rem = wid % per_bh, pair = rem / a.kpieces, piece = rem % a.kpieces;
-  const int kvh = bh % a.Hkv, b = bh / a.Hkv;
+  // (the 128-row instantiation keeps plain divisions: with the multiplier
+  // form its compiler output demotes the query fragments to scratch)
+  const int bh = R64 ? fdiv(wid, a.fd_pbh) : wid / per_bh, rem = wid - bh * per_bh;
+  const int pair = R64 ? fdiv(rem, a.fd_kp) : rem / a.kpieces, piece = rem - pair * a.kpieces;
+  const int b = R64 ? fdiv(bh, a.fd_hkv) : bh / a.Hkv, kvh = bh - b * a.Hkv;
   const int rows_total = a.S * a.g;
   const bool windowed = a.W > 0;
 
   auto tile_keys = [&](int qt, int& jlo, int& jhi) {
     const int r0 = qt * ROWS;
-    const int pmin = a.P0 + r0 / a.g, pmax = a.P0 + min(r0 + ROWS - 1, rows_total - 1) / a.g;
+    const int rl = min(r0 + ROWS - 1, rows_total - 1);
+    const int pmin = a.P0 + (R64 ? fdiv(r0, a.fd_g) : r0 / a.g), pmax = a.P0 + (R64 ? fdiv(rl, a.fd_g) : rl / a.g);
     jlo = (windowed ? max(0, pmin - a.W + 1) : 0) / BN;
     jhi = causal_limit<SPAN>(a, b, pmax - a.P0, pmax) / BN;
   };
@@ -1323,7 +1349,7 @@ k_prefill4(PrefillArgs a) {
   tile_keys(tl, jlo_l, jhi_l);
   if (ts >= 0) tile_keys(ts, jlo_s, jhi_s);
   const int nL = jhi_l - jlo_l + 1, nS = ts >= 0 ? jhi_s - jlo_s + 1 : 0, U = nL + nS;
-  auto ubound = [&](int j) { return (int)(((long long)j * U) / a.kpieces); };
+  auto ubound = [&](int j) { return R64 ? fdiv(j * U, a.fd_kp) : (int)(((long long)j * U) / a.kpieces); };
   const int u0 = ubound(piece), u1 = ubound(piece + 1);
 
   const size_t slice_off = (size_t)(b * a.Hkv + kvh) * a.ntiles * (size_t)(BN * D);
@@ -1357,8 +1383,9 @@ k_prefill4(PrefillArgs a) {
     const int rc = r < rows_total ? r : rows_total - 1;
     const int sq = rc / a.g;     // query index within the chunk
     const int pos = a.P0 + sq;   // its position in the sequence
-    const int pos_min = a.P0 + r0 / a.g;
-    const int pos_max = a.P0 + min(r0 + ROWS - 1, rows_total - 1) / a.g;
+    const int rl = min(r0 + ROWS - 1, rows_total - 1);
+    const int pos_min = a.P0 + (R64 ? fdiv(r0, a.fd_g) : r0 / a.g);
+    const int pos_max = a.P0 + (R64 ? fdiv(rl, a.fd_g) : rl / a.g);
     const int lim = causal_limit<SPAN>(a, b, sq, pos);                      // this lane's row's last visible key
     const int lim_min = causal_limit<SPAN>(a, b, pos_min - a.P0, pos_min);  // the smallest limit of the tile
     const int nt = je - jb + 1;
@@ -2750,6 +2777,15 @@ void fill_rope_rev(RopeRev* r, int head_dim, double theta) {
     r->rev[f] = f < head_dim / 2 ? std::pow(theta, -2.0 * (double)f / (double)head_dim) / two_pi : 0.0;
 }
 
+// FastDiv constants of divisor d >= 1 (see fdiv).
+static FastDiv make_fastdiv(int d) {
+  unsigned L = 0;
+  while ((1ull << L) < (unsigned long long)d) ++L;
+  const unsigned s = 31 + L;
+  const unsigned long long m = ((1ull << s) + (unsigned long long)d - 1) / (unsigned long long)d;
+  return FastDiv{(unsigned)m, s};
+}
+
 // Key tiles a query tile visits (same rule as the kernel; P0 = position of query 0).
 static void prefill_tile_keys(int qt, int S, int g, int W, int BN, int rows, int P0, int& jlo, int& jhi) {
   const int rows_total = S * g, r0 = qt * rows;
@@ -2846,7 +2882,10 @@ PrefillPlan plan_prefill(int B, int S, int Hq, int Hkv, int D, int W, int P0) {
       int kmax =
           rows == 64 ? 1 : (int)std::max<long>(1, std::min<long>(std::min<long>(kPrefillSlots / groups, umax), 64));
       if (rows != 64 && prefill_kpieces_override()) kmax = std::min(prefill_kpieces_override(), umax);
-      const int kforced = rows == 64 ? 0 : prefill_kpieces_override();
+      // the kernels cut a unit's key tiles at j * U / kpieces (j <= kpieces,
+      // U <= 2 * ntiles) in 31-bit arithmetic
+      kmax = (int)std::min<long long>(kmax, std::max<long long>(1, ((1LL << 31) - 1) / (2LL * p.ntiles + 2)));
+      const int kforced = rows == 64 ? 0 : std::min(prefill_kpieces_override(), kmax);
       for (int k = 1; k <= kmax; ++k) {
         if (kforced && k != std::min(kforced, umax)) continue;
         const double rounds = std::ceil((double)groups * k / kPrefillSlots);
@@ -2913,6 +2952,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Prof
   a.kpieces = pl.kpieces;
   a.qscale = p.scale * kLog2e * p.k_scale;
   a.vscale = p.v_scale;
+  a.fd_g = make_fastdiv(pl.g);
+  a.fd_kp = make_fastdiv(pl.kpieces);
+  a.fd_pbh = make_fastdiv(pl.npair * pl.kpieces);
+  a.fd_hkv = make_fastdiv(p.Hkv);
   fill_rope_rev(&a.rope, p.D, p.theta);
   const dim3 grid_k(2 * pl.ntiles, p.Hkv, p.B);
   const dim3 grid_a((unsigned)((long)p.B * p.Hkv * pl.npair * pl.kpieces));
